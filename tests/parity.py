@@ -1,0 +1,148 @@
+"""Forward/backward comparison with the near-threshold excuse rule.
+
+pix_to_face must match exactly. A pixel whose face list differs is excused
+only when every face involved sits at a near-threshold point: its inclusion
+flips when blur_radius moves by +-1e-6 (its squared distance is within 1e-6
+of blur_radius), its depth is within 1e-6 of another candidate's depth (an
+order swap, including across the K-th slot), or its depth is within 1e-6 of
+zero (the z <= 0 skip). Values (zbuf, bary, dists) are compared on slots whose
+face matches; padding must be exactly -1.
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+DELTA = 1e-6
+
+
+def _rows(a, K, trailing=0):
+    a = np.asarray(a)
+    return a.reshape((-1, K) + a.shape[a.ndim - trailing:] if trailing else (-1, K))
+
+
+def compare_forward(ref, got, K: int, atol: float = 1e-5, excuse=None):
+    rp, rz, rb, rd = ref
+    gp, gz, gb, gd = got
+    rp, gp = _rows(rp, K), _rows(gp, K)
+    rz, gz = _rows(rz, K), _rows(gz, K)
+    rd, gd = _rows(rd, K), _rows(gd, K)
+    rb, gb = _rows(rb, K, 1), _rows(gb, K, 1)
+    assert rp.shape == gp.shape, (rp.shape, gp.shape)
+    mism = np.nonzero((rp != gp).any(axis=1))[0]
+    excused, unexcused = [], []
+    for r in mism:
+        ok = excuse is not None and excuse(int(r), rp[r], gp[r], rz[r], gz[r])
+        (excused if ok else unexcused).append(int(r))
+    same = (rp == gp) & (rp >= 0)
+    pad = (rp == gp) & (rp < 0)
+
+    def maxerr(a, b, m):
+        if not m.any():
+            return 0.0
+        return float(np.max(np.abs(a[m].astype(np.float64) - b[m].astype(np.float64))))
+
+    rep = {
+        "pixels": int(rp.shape[0]),
+        "excused": excused,
+        "unexcused": unexcused,
+        "max_err_zbuf": maxerr(rz, gz, same),
+        "max_err_bary": maxerr(rb, gb, same[..., None].repeat(3, -1)),
+        "max_err_dists": maxerr(rd, gd, same),
+        "padding_ok": bool(np.all(gz[pad] == -1) and np.all(gb[pad] == -1) and np.all(gd[pad] == -1)),
+        "filled_slots": int(same.sum()),
+    }
+    rep["values_ok"] = (rep["max_err_zbuf"] <= atol and rep["max_err_bary"] <= atol
+                        and rep["max_err_dists"] <= atol)
+    return rep
+
+
+def assert_forward_parity(rep, max_excused_frac: float = 1e-4):
+    assert not rep["unexcused"], f"unexcused pix_to_face mismatches at rows {rep['unexcused'][:20]}"
+    assert len(rep["excused"]) <= max_excused_frac * rep["pixels"], \
+        f"{len(rep['excused'])} excused pixels of {rep['pixels']}"
+    assert rep["padding_ok"], "padding slots are not exactly -1"
+    assert rep["values_ok"], {k: rep[k] for k in ("max_err_zbuf", "max_err_bary", "max_err_dists")}
+
+
+def _diff_faces(ref_faces, got_faces):
+    """Faces that are missing on one side, or present on both in other slots."""
+    out = set(int(f) for f in set(ref_faces.tolist()) ^ set(got_faces.tolist()) if f >= 0)
+    for k, (a, b) in enumerate(zip(ref_faces, got_faces)):
+        if a != b:
+            if a >= 0:
+                out.add(int(a))
+            if b >= 0:
+                out.add(int(b))
+    return out
+
+
+def oracle_excuse(oracle, w_verts, w_faces, w_offsets, H, W, blur, pixel_ids=None, delta=DELTA):
+    """Excuse function backed by the binary32 oracle: pixel rows index
+    pixel_ids (or all pixels in order when pixel_ids is None)."""
+    offsets = np.asarray(w_offsets)
+
+    def fn(row, ref_faces, got_faces, ref_z, got_z):
+        pid = int(row if pixel_ids is None else pixel_ids[row])
+        n = pid // (H * W)
+        Kall = max(1, int(offsets[n + 1] - offsets[n]))
+        runs = {}
+        for tag, b in (("mid", blur), ("lo", max(0.0, blur - delta)), ("hi", blur + delta)):
+            p, z, _, _ = oracle.rasterize(w_verts, w_faces, offsets, H, W, Kall, b,
+                                          pixels=np.asarray([pid]))
+            m = p[0] >= 0
+            runs[tag] = dict(zip(p[0][m].tolist(), z[0][m].tolist()))
+        near_blur = set(runs["hi"]) - set(runs["lo"])
+        zmap = dict(runs["mid"])
+        for f, z in zip(got_faces.tolist(), got_z.tolist()):
+            if f >= 0 and f not in zmap:
+                zmap[f] = z
+        for f in _diff_faces(ref_faces, got_faces):
+            if f in near_blur:
+                continue
+            zf = zmap.get(f)
+            if zf is None:
+                return False
+            if abs(zf) <= delta:
+                continue
+            if any(abs(zf - zg) <= delta for g, zg in zmap.items() if g != f):
+                continue
+            return False
+        return True
+
+    return fn
+
+
+def exact_excuse(details, N, H, W, blur, delta=DELTA):
+    """Excuse function backed by exact per-face details (tests/exact_raster.py)."""
+    from fractions import Fraction as Fr
+
+    blur = Fr(float(np.float32(blur)))
+    d = Fr(delta)
+
+    def fn(row, ref_faces, got_faces, ref_z, got_z):
+        n, rem = divmod(row, H * W)
+        i, j = divmod(rem, W)
+        per_face = details[(n, i, j)]
+        cand_z = {f: r["z"] for f, r in per_face.items() if r["candidate"]}
+        for f in _diff_faces(ref_faces, got_faces):
+            r = per_face.get(f)
+            if r is None:
+                return False
+            if abs(r["d2"] - blur) <= d:
+                continue
+            if abs(r["z"]) <= d:
+                continue
+            if any(abs(r["z"] - zg) <= d for g, zg in cand_z.items() if g != f):
+                continue
+            return False
+        return True
+
+    return fn
+
+
+def rel_l2(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    den = np.linalg.norm(b)
+    return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
