@@ -24,7 +24,8 @@
  * The pages leave the arithmetic conventions open; the ones used here are:
  *   pixel centre     px = fl(fl((2j+1)/W) - 1), py = fl(fl((2i+1)/H) - 1), no axis flip;
  *   barycentrics     edge functions of (vertex - pixel) differences, times 1/A;
- *   inside           strictly inside: all three barycentrics > 0;
+ *   inside           strictly inside: all three barycentrics > 0 (and the centre
+ *                    in the face's closed bounding box, implied in exact arithmetic);
  *   distance         squared distance to the nearest of the three closed edges;
  *   inclusion        inside, or squared distance strictly below blur_radius;
  *   depth            z from barycentrics clipped to [0,1] and renormalised,
@@ -96,7 +97,20 @@ static int SFX(eval_face)(const R* verts, int64_t V, const int64_t* faces, int64
     s->w[1] = s->dx[2] * s->dy[0] - s->dy[2] * s->dx[0];
     s->w[2] = s->dx[0] * s->dy[1] - s->dy[0] * s->dx[1];
     for (int k = 0; k < 3; ++k) s->b[k] = s->w[k] * s->invA;
-    s->inside = (s->b[0] > (R)0) && (s->b[1] > (R)0) && (s->b[2] > (R)0);
+    /* A point strictly inside the triangle lies in its closed bounding box;
+     * requiring it too changes nothing in exact arithmetic and keeps rounding
+     * noise of near-degenerate faces from reaching beyond that box. */
+    {
+        R xmin = s->x[0], xmax = s->x[0], ymin = s->y[0], ymax = s->y[0];
+        for (int k = 1; k < 3; ++k) {
+            if (s->x[k] < xmin) xmin = s->x[k];
+            if (s->x[k] > xmax) xmax = s->x[k];
+            if (s->y[k] < ymin) ymin = s->y[k];
+            if (s->y[k] > ymax) ymax = s->y[k];
+        }
+        int in_box = (px >= xmin) && (px <= xmax) && (py >= ymin) && (py <= ymax);
+        s->inside = in_box && (s->b[0] > (R)0) && (s->b[1] > (R)0) && (s->b[2] > (R)0);
+    }
 
     /* Squared distance to each closed edge (v[e], v[e+1]); keep the first minimum. */
     for (int e = 0; e < 3; ++e) {
