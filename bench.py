@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark: forward+backward K-nearest-face mesh rasterization on one MI355X.
+
+One step = rasterize_meshes_fwd + rasterize_meshes_bwd (every stage of the
+path: face setup, bin count, scan, bin fill, fine raster, gradient zeroing,
+backward) over one batch of seeded synthetic meshes already resident in HBM.
+The default workload is a heterogeneous batch of 16 icospheres (levels 3-6,
+1280-81920 triangles each) at 256x256, K = 10, blur_radius = 1e-4.
+
+Prints one JSON line: throughput in Mpixel*K slots per second, the roofline
+of the dominant kernel (timed with HIP events on its own stream inside the
+timed region), and the CPU oracle timed on a bounded pixel sample of the same
+workload on this host.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 3] [--workload hetero16_256]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, GB/s
+
+METRIC = "forward+backward Mpixels*K/s at 1 MI355X; % of fp32-VALU/HBM roofline"
+
+
+def algorithmic_bytes(w, filled_slots, live_faces, grads):
+    """Bytes each kernel must move at minimum (per launch)."""
+    slots = w.slots
+    fine = 28 * slots + 36 * live_faces  # outputs + face geometry read once
+    g = (4 if "zbuf" in grads else 0) + (12 if "bary" in grads else 0) + (4 if "dists" in grads else 0)
+    bwd = 8 * slots + g * filled_slots + 24 * w.F + 12 * w.V + 12 * w.V
+    fwd_total = 28 * slots + 24 * w.F + 12 * w.V
+    return {"fine_raster": fine, "backward_pixels": bwd, "fwd_total": fwd_total, "bwd_total": bwd}
+
+
+def cpu_baseline(w, grads_np, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the workload's pixels."""
+    import numpy as np
+
+    import oracle
+    from workloads import sample_pixels
+
+    rng = np.random.Generator(np.random.PCG64(99))
+    done_pix = 0
+    t_fwd = t_bwd = 0.0
+    batch = 256
+    while t_fwd + t_bwd < seconds:
+        pix = np.unique(rng.integers(0, w.pixels, batch))
+        t0 = time.perf_counter()
+        p2f = oracle.rasterize(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur, pixels=pix)[0]
+        t1 = time.perf_counter()
+        sel = {k: (None if v is None else v.reshape((w.pixels, w.K) + v.shape[4:])[pix]) for k, v in grads_np.items()}
+        oracle.backward(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur, p2f,
+                        sel["zbuf"], sel["bary"], sel["dists"], pixels=pix)
+        t2 = time.perf_counter()
+        t_fwd += t1 - t0
+        t_bwd += t2 - t1
+        done_pix += len(pix)
+        batch = min(batch * 2, 65536)
+    slots = done_pix * w.K
+    return {
+        "value": slots / (t_fwd + t_bwd) / 1e6,
+        "unit": "Mpix*K/s",
+        "cores": oracle.num_threads(),
+        "kind": "oracle",
+        "sample": f"{done_pix} uniformly drawn pixels of the same workload ({slots} slots), "
+                  f"fwd {t_fwd:.1f} s + bwd {t_bwd:.1f} s on the host CPU",
+        "fwd_value": slots / t_fwd / 1e6,
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="hetero16_256")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no multi-GPU mode "
+              "(each image is independent; see the sharding notes in the design document)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import differentiable_mesh_rasterization_amd as dmr
+    from workloads import make_workload, upstream_grads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    w = make_workload(args.workload)
+    gnp = upstream_grads(w)
+    stream = torch.cuda.current_stream(dev)
+
+    verts = torch.from_numpy(w.verts).to(dev)
+    faces = torch.from_numpy(w.faces).to(dev)
+    offsets = torch.from_numpy(w.offsets).to(dev)
+    shape = (w.N, w.H, w.W, w.K)
+    p2f = torch.empty(shape, dtype=torch.int64, device=dev)
+    zbuf = torch.empty(shape, dtype=torch.float32, device=dev)
+    bary = torch.empty(shape + (3,), dtype=torch.float32, device=dev)
+    dists = torch.empty(shape, dtype=torch.float32, device=dev)
+    gv = torch.empty_like(verts)
+    g = {k: (None if v is None else torch.from_numpy(v).to(dev)) for k, v in gnp.items()}
+    ws = dmr.Workspace(dev)
+    ws.ensure(dmr.dmr_workspace_size_hint(w.N, w.F, w.H, w.W, w.K, w.blur))
+    bwd_ws = torch.empty(max(1, dmr.dmr_bwd_workspace_size(w.N, w.F, w.V, w.H, w.W, w.K)), dtype=torch.uint8,
+                         device=dev)
+
+    def step():
+        dmr.rasterize_meshes_fwd(verts, faces, offsets, w.H, w.W, w.K, w.blur, p2f, zbuf, bary, dists, ws.buf)
+        dmr.rasterize_meshes_bwd(verts, faces, offsets, w.H, w.W, w.K, p2f, g["zbuf"], g["bary"], g["dists"], gv,
+                                 bwd_ws)
+
+    step()
+    stats = ws.grow()  # size the workspace so every bin list fits
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    stats = dmr.dmr_workspace_stats(ws.buf)
+    filled = int((p2f >= 0).sum().item())
+
+    if not args.no_kernel_timing:
+        dmr.set_kernel_timing(True)
+        dmr.reset_kernel_timing()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    kt = dmr.kernel_timing() if not args.no_kernel_timing else {}
+    dmr.set_kernel_timing(False)
+    ms_events = ev0.elapsed_time(ev1) / args.steps
+    ms_wall = (t1 - t0) * 1e3 / args.steps
+    ms_per_step = max(ms_events, ms_wall)
+    value = w.slots / (ms_per_step * 1e-3) / 1e6
+
+    alg = algorithmic_bytes(w, filled, stats["live_faces"], w.grads)
+    kernels = {name: {"avg_us": (ms / n * 1e3) if n else None, "launches": n} for name, (ms, n) in kt.items()}
+    roofline = None
+    if kt:
+        dominant = max(("fine_raster", "backward_pixels"), key=lambda k: kt[k][0])
+        ms, n = kt[dominant]
+        avg_s = ms / n * 1e-3
+        achieved = alg[dominant] / avg_s / 1e9
+        roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "algorithmic_bytes_per_launch": alg[dominant], "avg_launch_us": round(avg_s * 1e6, 2)}
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "Mpix*K/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "N": w.N, "H": w.H, "W": w.W, "K": w.K, "blur_radius": w.blur,
+                   "faces": w.F, "verts": w.V, "slots": w.slots, "filled_slots": filled,
+                   "grads": list(w.grads), "parallelism": "single GPU"},
+        "roofline": roofline,
+        "kernels": kernels,
+        "fwd_bwd_hbm_frac": round((alg["fwd_total"] + alg["bwd_total"]) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "workspace": {k: stats[k] for k in ("required_bytes", "bin_entries", "overflow_bins", "live_faces")},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, gnp, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

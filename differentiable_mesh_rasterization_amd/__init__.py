@@ -1,0 +1,309 @@
+"""MI355X-native K-nearest-face mesh rasterizer (forward and backward).
+
+A thin ctypes binding over libdmr.so, whose C ABI is declared in
+include/dmr.h. The functions below only marshal torch tensors (device
+memory) and the current HIP stream into that ABI: every step of the
+computation runs in the library's HIP kernels. There is no CPU fallback: if
+libdmr.so is missing, every call raises.
+
+    rasterize_meshes_fwd / rasterize_meshes_bwd   the two C-ABI entry points
+    rasterize_meshes                              autograd-aware convenience
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdmr.so")
+
+DMR_MAX_K = 64
+STATUS = {0: "DMR_SUCCESS", 1: "DMR_ERROR_INVALID_VALUE", 2: "DMR_ERROR_WORKSPACE_TOO_SMALL",
+          3: "DMR_ERROR_HIP", 4: "DMR_ERROR_UNSUPPORTED"}
+EXPORTED = [
+    "rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
+    "dmr_bwd_workspace_size", "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
+    "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_kernel_timing", "dmr_reset_kernel_timing",
+]
+
+
+class DmrError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class dmr_stats(ctypes.Structure):
+    _fields_ = [("required_bytes", ctypes.c_int64), ("bin_entries", ctypes.c_int64),
+                ("bin_capacity", ctypes.c_int64), ("bins", ctypes.c_int64),
+                ("overflow_bins", ctypes.c_int64), ("live_faces", ctypes.c_int64),
+                ("flags", ctypes.c_uint32), ("reserved", ctypes.c_uint32)]
+
+
+_lib = None
+
+
+def lib(path: Optional[str] = None):
+    """Loads libdmr.so (once) and declares the C signatures."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIB_PATH
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is not built; run `python -m differentiable_mesh_rasterization_amd.build`")
+    L = ctypes.CDLL(p)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    L.rasterize_meshes_fwd.restype = ctypes.c_int
+    L.rasterize_meshes_fwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
+                                       P, P, P, P, P, SZ, P]
+    L.rasterize_meshes_bwd.restype = ctypes.c_int
+    L.rasterize_meshes_bwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    L.dmr_workspace_min_size.restype = SZ
+    L.dmr_workspace_min_size.argtypes = [I64, I64, I32, I32]
+    L.dmr_workspace_size_hint.restype = SZ
+    L.dmr_workspace_size_hint.argtypes = [I64, I64, I32, I32, I32, ctypes.c_float]
+    L.dmr_bwd_workspace_size.restype = SZ
+    L.dmr_bwd_workspace_size.argtypes = [I64, I64, I64, I32, I32, I32]
+    L.dmr_workspace_stats.restype = ctypes.c_int
+    L.dmr_workspace_stats.argtypes = [P, ctypes.POINTER(dmr_stats), P]
+    L.dmr_status_string.restype = ctypes.c_char_p
+    L.dmr_status_string.argtypes = [ctypes.c_int]
+    L.dmr_kernel_count.restype = I32
+    L.dmr_kernel_count.argtypes = []
+    L.dmr_kernel_name.restype = ctypes.c_char_p
+    L.dmr_kernel_name.argtypes = [I32]
+    L.dmr_set_kernel_timing.restype = ctypes.c_int
+    L.dmr_set_kernel_timing.argtypes = [I32]
+    L.dmr_kernel_timing.restype = ctypes.c_int
+    L.dmr_kernel_timing.argtypes = [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
+    L.dmr_reset_kernel_timing.restype = ctypes.c_int
+    L.dmr_reset_kernel_timing.argtypes = []
+    if path is None:
+        _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().dmr_status_string(int(status)).decode()
+
+
+dmr_status_string = status_string
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(device: torch.device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(t: torch.Tensor, name: str, dtype, device, shape=None, optional=False):
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+# ----------------------------------------------------------------------------
+# workspace sizes and statistics
+# ----------------------------------------------------------------------------
+
+def dmr_workspace_min_size(N: int, F: int, H: int, W: int) -> int:
+    return int(lib().dmr_workspace_min_size(N, F, H, W))
+
+
+def dmr_workspace_size_hint(N: int, F: int, H: int, W: int, K: int, blur_radius: float) -> int:
+    return int(lib().dmr_workspace_size_hint(N, F, H, W, K, blur_radius))
+
+
+def dmr_bwd_workspace_size(N: int, F: int, V: int, H: int, W: int, K: int) -> int:
+    return int(lib().dmr_bwd_workspace_size(N, F, V, H, W, K))
+
+
+def dmr_workspace_stats(workspace: torch.Tensor) -> dict:
+    s = dmr_stats()
+    rc = lib().dmr_workspace_stats(_ptr(workspace), ctypes.byref(s), _stream_handle(workspace.device))
+    if rc != 0:
+        raise DmrError("dmr_workspace_stats", rc)
+    return {f: getattr(s, f) for f, _ in dmr_stats._fields_ if f != "reserved"}
+
+
+# ----------------------------------------------------------------------------
+# the two entry points
+# ----------------------------------------------------------------------------
+
+def rasterize_meshes_fwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
+                         H: int, W: int, K: int, blur_radius: float,
+                         pix_to_face: torch.Tensor, zbuf: torch.Tensor, bary: torch.Tensor,
+                         dists: torch.Tensor, workspace: torch.Tensor) -> None:
+    """C-ABI forward call on preallocated device tensors (include/dmr.h)."""
+    dev = verts.device
+    N = mesh_face_offsets.shape[0] - 1
+    _check(verts, "verts", torch.float32, dev)
+    _check(faces, "faces", torch.int64, dev)
+    _check(mesh_face_offsets, "mesh_face_offsets", torch.int64, dev)
+    shape = (N, H, W, K)
+    _check(pix_to_face, "pix_to_face", torch.int64, dev, shape)
+    _check(zbuf, "zbuf", torch.float32, dev, shape)
+    _check(bary, "bary", torch.float32, dev, shape + (3,))
+    _check(dists, "dists", torch.float32, dev, shape)
+    _check(workspace, "workspace", torch.uint8, dev)
+    rc = lib().rasterize_meshes_fwd(
+        _ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
+        H, W, K, float(blur_radius), _ptr(pix_to_face), _ptr(zbuf), _ptr(bary), _ptr(dists),
+        _ptr(workspace), workspace.numel(), _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("rasterize_meshes_fwd", rc)
+
+
+def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
+                         H: int, W: int, K: int, pix_to_face: torch.Tensor,
+                         grad_zbuf: Optional[torch.Tensor], grad_bary: Optional[torch.Tensor],
+                         grad_dists: Optional[torch.Tensor], grad_verts: torch.Tensor,
+                         workspace: Optional[torch.Tensor] = None) -> None:
+    """C-ABI backward call on preallocated device tensors (include/dmr.h)."""
+    dev = verts.device
+    N = mesh_face_offsets.shape[0] - 1
+    shape = (N, H, W, K)
+    _check(verts, "verts", torch.float32, dev)
+    _check(faces, "faces", torch.int64, dev)
+    _check(mesh_face_offsets, "mesh_face_offsets", torch.int64, dev)
+    _check(pix_to_face, "pix_to_face", torch.int64, dev, shape)
+    _check(grad_zbuf, "grad_zbuf", torch.float32, dev, shape, optional=True)
+    _check(grad_bary, "grad_bary", torch.float32, dev, shape + (3,), optional=True)
+    _check(grad_dists, "grad_dists", torch.float32, dev, shape, optional=True)
+    _check(grad_verts, "grad_verts", torch.float32, dev, tuple(verts.shape))
+    _check(workspace, "workspace", torch.uint8, dev, optional=True)
+    rc = lib().rasterize_meshes_bwd(
+        _ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
+        H, W, K, _ptr(pix_to_face), _ptr(grad_zbuf), _ptr(grad_bary), _ptr(grad_dists), _ptr(grad_verts),
+        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("rasterize_meshes_bwd", rc)
+
+
+# ----------------------------------------------------------------------------
+# convenience: allocation + autograd
+# ----------------------------------------------------------------------------
+
+class Workspace:
+    """Grow-only forward workspace for one device. The first call on a shape
+    uses the library's size hint; calls made with too small a workspace stay
+    exact (overflowing bins take the slow path), and `grow()` reads the size
+    the last call needed."""
+
+    def __init__(self, device):
+        self.device = torch.device(device)
+        self.buf = torch.empty(0, dtype=torch.uint8, device=self.device)
+
+    def ensure(self, nbytes: int) -> torch.Tensor:
+        if self.buf.numel() < nbytes:
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+    def grow(self) -> dict:
+        stats = dmr_workspace_stats(self.buf)
+        self.ensure(stats["required_bytes"])
+        return stats
+
+
+_workspaces = {}
+
+
+def workspace_for(device) -> Workspace:
+    device = torch.device(device)
+    if device not in _workspaces:
+        _workspaces[device] = Workspace(device)
+    return _workspaces[device]
+
+
+def _alloc_outputs(N, H, W, K, device):
+    return (torch.empty((N, H, W, K), dtype=torch.int64, device=device),
+            torch.empty((N, H, W, K), dtype=torch.float32, device=device),
+            torch.empty((N, H, W, K, 3), dtype=torch.float32, device=device),
+            torch.empty((N, H, W, K), dtype=torch.float32, device=device))
+
+
+class _RasterizeMeshes(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, verts, faces, offsets, H, W, K, blur_radius):
+        N = offsets.shape[0] - 1
+        out = _alloc_outputs(N, H, W, K, verts.device)
+        ws = workspace_for(verts.device)
+        buf = ws.ensure(dmr_workspace_size_hint(N, faces.shape[0], H, W, K, blur_radius))
+        rasterize_meshes_fwd(verts, faces, offsets, H, W, K, blur_radius, *out, buf)
+        ctx.save_for_backward(verts, faces, offsets, out[0])
+        ctx.dims = (H, W, K)
+        ctx.mark_non_differentiable(out[0])
+        return out
+
+    @staticmethod
+    def backward(ctx, g_p2f, g_zbuf, g_bary, g_dists):
+        verts, faces, offsets, p2f = ctx.saved_tensors
+        H, W, K = ctx.dims
+        grad_verts = torch.empty_like(verts)
+
+        def c(g):
+            return None if g is None else g.contiguous()
+
+        rasterize_meshes_bwd(verts, faces, offsets, H, W, K, p2f, c(g_zbuf), c(g_bary), c(g_dists), grad_verts)
+        return grad_verts, None, None, None, None, None, None
+
+
+def rasterize_meshes(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
+                     image_size: Tuple[int, int], faces_per_pixel: int = 1, blur_radius: float = 0.0):
+    """Rasterizes a packed batch of meshes on the GPU.
+
+    verts [V,3] float32 (x, y NDC, z depth), faces [F,3] int64, mesh_face_offsets
+    [N+1] int64. Returns (pix_to_face, zbuf, bary, dists); zbuf, bary and dists
+    are differentiable with respect to verts."""
+    H, W = image_size
+    return _RasterizeMeshes.apply(verts, faces, mesh_face_offsets, int(H), int(W), int(faces_per_pixel),
+                                  float(blur_radius))
+
+
+# ----------------------------------------------------------------------------
+# per-kernel timing (measurement only)
+# ----------------------------------------------------------------------------
+
+def kernel_names():
+    L = lib()
+    return [L.dmr_kernel_name(i).decode() for i in range(L.dmr_kernel_count())]
+
+
+def set_kernel_timing(enable: bool) -> None:
+    rc = lib().dmr_set_kernel_timing(1 if enable else 0)
+    if rc != 0:
+        raise DmrError("dmr_set_kernel_timing", rc)
+
+
+def reset_kernel_timing() -> None:
+    rc = lib().dmr_reset_kernel_timing()
+    if rc != 0:
+        raise DmrError("dmr_reset_kernel_timing", rc)
+
+
+def kernel_timing() -> dict:
+    """{kernel name: (total ms, launches)} since the last reset."""
+    L = lib()
+    out = {}
+    for i, name in enumerate(kernel_names()):
+        ms, n = ctypes.c_double(), ctypes.c_int64()
+        rc = L.dmr_kernel_timing(i, ctypes.byref(ms), ctypes.byref(n))
+        if rc != 0:
+            raise DmrError("dmr_kernel_timing", rc)
+        out[name] = (ms.value, n.value)
+    return out

@@ -1,0 +1,248 @@
+// C ABI of libdmr (include/dmr.h): host-side validation, workspace layout,
+// launch sequencing and optional per-kernel event timing.
+#include <math.h>
+#include <string.h>
+
+#include <mutex>
+#include <vector>
+
+#include "dmr_internal.h"
+
+namespace dmr {
+
+// ---------------------------------------------------------------------------
+// per-kernel event timing
+// ---------------------------------------------------------------------------
+namespace {
+
+struct Pending {
+    hipEvent_t start, stop;
+};
+
+struct Timing {
+    bool enabled = false;
+    std::vector<Pending> pending[kKernelCount];
+    std::vector<hipEvent_t> pool;
+    double total_ms[kKernelCount] = {};
+    int64_t launches[kKernelCount] = {};
+    hipEvent_t open_start[kKernelCount] = {};
+};
+
+Timing g_timing;
+std::mutex g_timing_mu;
+
+const char* const kKernelNames[kKernelCount] = {
+    "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "fine_raster", "zero_grad", "backward_pixels",
+};
+
+hipEvent_t take_event() {
+    if (!g_timing.pool.empty()) {
+        hipEvent_t e = g_timing.pool.back();
+        g_timing.pool.pop_back();
+        return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+}
+
+hipError_t drain(int id) {
+    for (auto& p : g_timing.pending[id]) {
+        hipError_t err = hipEventSynchronize(p.stop);
+        if (err != hipSuccess) return err;
+        float ms = 0.0f;
+        err = hipEventElapsedTime(&ms, p.start, p.stop);
+        if (err != hipSuccess) return err;
+        g_timing.total_ms[id] += ms;
+        g_timing.launches[id] += 1;
+        g_timing.pool.push_back(p.start);
+        g_timing.pool.push_back(p.stop);
+    }
+    g_timing.pending[id].clear();
+    return hipSuccess;
+}
+
+}  // namespace
+
+void timing_begin(KernelId id, hipStream_t s) {
+    if (!g_timing.enabled) return;
+    hipEvent_t e = take_event();
+    if (e && hipEventRecord(e, s) == hipSuccess) g_timing.open_start[id] = e;
+}
+
+void timing_end(KernelId id, hipStream_t s) {
+    if (!g_timing.enabled || !g_timing.open_start[id]) return;
+    hipEvent_t e = take_event();
+    if (e && hipEventRecord(e, s) == hipSuccess) g_timing.pending[id].push_back({g_timing.open_start[id], e});
+    g_timing.open_start[id] = nullptr;
+}
+
+}  // namespace dmr
+
+using namespace dmr;
+
+namespace {
+
+bool mul_overflows(int64_t a, int64_t b, int64_t* out) {
+    if (a < 0 || b < 0) return true;
+    if (a != 0 && b > INT64_MAX / a) return true;
+    *out = a * b;
+    return false;
+}
+
+// Shared validation of the geometry arguments. Returns DMR_SUCCESS or the
+// status to report.
+dmr_status check_geometry(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                          const int64_t* off, int64_t N, int32_t H, int32_t W, int32_t K,
+                          int64_t* slots_out) {
+    if (V < 0 || F < 0 || N < 0) return DMR_ERROR_INVALID_VALUE;
+    if (H < 1 || W < 1 || K < 1) return DMR_ERROR_INVALID_VALUE;
+    if (H > DMR_MAX_IMAGE_SIDE || W > DMR_MAX_IMAGE_SIDE || K > DMR_MAX_K) return DMR_ERROR_UNSUPPORTED;
+    if (F > (int64_t)INT32_MAX - 1) return DMR_ERROR_UNSUPPORTED;  // face ids are 32-bit inside
+    if (V > INT64_MAX / 3) return DMR_ERROR_UNSUPPORTED;
+    int64_t pix, slots, slots3;
+    if (mul_overflows(N, (int64_t)H * W, &pix)) return DMR_ERROR_UNSUPPORTED;
+    if (mul_overflows(pix, K, &slots)) return DMR_ERROR_UNSUPPORTED;
+    if (mul_overflows(slots, 3, &slots3)) return DMR_ERROR_UNSUPPORTED;
+    if (F > 0 && faces == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (V > 0 && verts == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (N > 0 && off == nullptr) return DMR_ERROR_INVALID_VALUE;
+    *slots_out = slots;
+    return DMR_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dmr_status_string(dmr_status s) {
+    switch (s) {
+        case DMR_SUCCESS: return "success";
+        case DMR_ERROR_INVALID_VALUE: return "invalid argument";
+        case DMR_ERROR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case DMR_ERROR_HIP: return "HIP runtime error";
+        case DMR_ERROR_UNSUPPORTED: return "unsupported size or parameter";
+    }
+    return "unknown status";
+}
+
+size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W) {
+    if (N < 0 || F < 0 || H < 1 || W < 1 || H > DMR_MAX_IMAGE_SIDE || W > DMR_MAX_IMAGE_SIDE) return 0;
+    return fwd_layout(N, F, H, W).min_bytes;
+}
+
+size_t dmr_workspace_size_hint(int64_t N, int64_t F, int32_t H, int32_t W, int32_t K, float blur_radius) {
+    (void)K;
+    size_t base = dmr_workspace_min_size(N, F, H, W);
+    if (base == 0 || !(blur_radius >= 0.0f) || !isfinite(blur_radius)) return 0;
+    FwdLayout L = fwd_layout(N, F, H, W);
+    // Face boxes grow by the blur radius (in pixels: sqrt(blur) * side / 2);
+    // allow each face the bins of a box one blur diameter wider than a bin.
+    double rpx = sqrt((double)blur_radius) * 0.5 * (double)(H > W ? H : W);
+    double per_face = (1.0 + (2.0 * rpx + 2.0) / kBin) * (1.0 + (2.0 * rpx + 2.0) / kBin);
+    double entries = 2.0 * per_face * (double)F + 4.0 * (double)L.bins + 1024.0;
+    if (entries > (double)INT32_MAX) entries = (double)INT32_MAX;
+    return align_up(base + (size_t)entries * sizeof(int32_t), 256);
+}
+
+size_t dmr_bwd_workspace_size(int64_t N, int64_t F, int64_t V, int32_t H, int32_t W, int32_t K) {
+    (void)N; (void)F; (void)V; (void)H; (void)W; (void)K;
+    return 0;
+}
+
+dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
+                                float blur_radius, int64_t* pix_to_face, float* zbuf, float* bary,
+                                float* dists, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int64_t slots = 0;
+    dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
+    if (st != DMR_SUCCESS) return st;
+    if (!isfinite(blur_radius) || blur_radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
+    if (slots == 0) return DMR_SUCCESS;
+    if (!pix_to_face || !zbuf || !bary || !dists) return DMR_ERROR_INVALID_VALUE;
+    FwdLayout L = fwd_layout(N, F, H, W);
+    if (L.bins > (int64_t)UINT32_MAX) return DMR_ERROR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < L.min_bytes) return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    int64_t cap = (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t));
+    if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
+
+    FwdArgs a;
+    a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
+    a.H = H; a.W = W; a.K = K; a.blur = blur_radius;
+    a.pix_to_face = pix_to_face; a.zbuf = zbuf; a.bary = bary; a.dists = dists;
+    a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes;
+    a.L = L; a.capacity = cap; a.stream = stream;
+    return launch_forward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
+                                const int64_t* pix_to_face, const float* grad_zbuf, const float* grad_bary,
+                                const float* grad_dists, float* grad_verts, void* workspace,
+                                size_t workspace_bytes, hipStream_t stream) {
+    int64_t slots = 0;
+    dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
+    if (st != DMR_SUCCESS) return st;
+    if (V > 0 && grad_verts == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (slots > 0 && pix_to_face == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (workspace_bytes < dmr_bwd_workspace_size(N, F, V, H, W, K)) return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    if (V == 0) return DMR_SUCCESS;
+    BwdArgs a;
+    a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
+    a.H = H; a.W = W; a.K = K; a.pix_to_face = pix_to_face;
+    a.gz = grad_zbuf; a.gb = grad_bary; a.gd = grad_dists; a.grad_verts = grad_verts;
+    a.stream = stream;
+    (void)workspace;
+    return launch_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+dmr_status dmr_workspace_stats(const void* workspace, dmr_stats* out, hipStream_t stream) {
+    if (workspace == nullptr || out == nullptr) return DMR_ERROR_INVALID_VALUE;
+    WsHeader h;
+    if (hipMemcpyAsync(&h, workspace, sizeof(h), hipMemcpyDeviceToHost, stream) != hipSuccess)
+        return DMR_ERROR_HIP;
+    if (hipStreamSynchronize(stream) != hipSuccess) return DMR_ERROR_HIP;
+    out->required_bytes = h.required_bytes;
+    out->bin_entries = h.bin_entries;
+    out->bin_capacity = h.bin_capacity;
+    out->bins = h.bins;
+    out->overflow_bins = h.overflow_bins;
+    out->live_faces = h.live_faces;
+    out->flags = h.flags;
+    out->reserved = 0;
+    return DMR_SUCCESS;
+}
+
+int32_t dmr_kernel_count(void) { return kKernelCount; }
+
+const char* dmr_kernel_name(int32_t id) {
+    if (id < 0 || id >= kKernelCount) return "";
+    return kKernelNames[id];
+}
+
+dmr_status dmr_set_kernel_timing(int32_t enable) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing.enabled = enable != 0;
+    return DMR_SUCCESS;
+}
+
+dmr_status dmr_kernel_timing(int32_t id, double* total_ms, int64_t* launches) {
+    if (id < 0 || id >= kKernelCount || !total_ms || !launches) return DMR_ERROR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (drain(id) != hipSuccess) return DMR_ERROR_HIP;
+    *total_ms = g_timing.total_ms[id];
+    *launches = g_timing.launches[id];
+    return DMR_SUCCESS;
+}
+
+dmr_status dmr_reset_kernel_timing(void) {
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    for (int id = 0; id < kKernelCount; ++id) {
+        if (drain(id) != hipSuccess) return DMR_ERROR_HIP;
+        g_timing.total_ms[id] = 0.0;
+        g_timing.launches[id] = 0;
+    }
+    return DMR_SUCCESS;
+}
+
+}  // extern "C"

@@ -1,0 +1,207 @@
+// Internal definitions shared by the HIP translation units of libdmr.
+//
+// Everything here is gfx950 device code or host-side layout arithmetic for
+// the K-nearest-face rasterizer declared in include/dmr.h. The per-pair
+// evaluation is written so that every binary32 operation happens in the
+// order the library's conventions fix (see dmr.h); the translation units are
+// compiled with -ffp-contract=off so that no multiply-add is fused, and
+// binary32 division and square root are correctly rounded (hipcc's default).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/dmr.h"
+
+namespace dmr {
+
+// Side of a coarse bin in pixels; the fine pass gives each bin one
+// 256-thread workgroup, one pixel per thread.
+constexpr int kBin = 16;
+constexpr int kBinPixels = kBin * kBin;
+constexpr int kFineThreads = kBinPixels;
+
+// Per-face record written by the setup pass and read by the fine pass
+// (80 bytes, five 16-byte vectors). A face that can never be a candidate
+// (degenerate, all depths <= 0, no pixel centre near it, bad vertex index)
+// has face == -1 and an empty pixel box.
+struct alignas(16) FaceRec {
+    float x0, y0, x1, y1;
+    float x2, y2, z0, z1;
+    float z2, invA, il0, il1;      // invA = 1/A; il_e = 1/|edge e|^2, edges (0,1) (1,2) (2,0)
+    float il2, xmin, xmax, ymin;   // closed xy bounding box of the three vertices
+    float ymax;
+    int32_t face;                  // global face index, or -1
+    int32_t box_lo;                // first pixel column | first pixel row << 16
+    int32_t box_hi;                // last pixel column | last pixel row << 16
+};
+static_assert(sizeof(FaceRec) == 80, "FaceRec layout");
+
+// Workspace header (first 256 bytes of the forward workspace).
+struct WsHeader {
+    int64_t required_bytes;
+    int64_t bin_entries;
+    int64_t bin_capacity;
+    int64_t bins;
+    int64_t overflow_bins;
+    int64_t live_faces;
+    uint32_t flags;
+    uint32_t reserved;
+    int64_t pad[25];
+};
+static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
+
+// Forward workspace layout; every section starts on a 256-byte boundary.
+struct FwdLayout {
+    int64_t bins, nbx, nby;
+    size_t off_records, off_count, off_offset, off_cursor, off_entries;
+    size_t min_bytes;
+};
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W) {
+    FwdLayout L;
+    L.nbx = (W + kBin - 1) / kBin;
+    L.nby = (H + kBin - 1) / kBin;
+    L.bins = N * L.nbx * L.nby;
+    size_t o = sizeof(WsHeader);
+    L.off_records = o;
+    o = align_up(o + (size_t)F * sizeof(FaceRec), 256);
+    L.off_count = o;
+    o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.off_offset = o;
+    o = align_up(o + (size_t)(L.bins + 1) * sizeof(int64_t), 256);
+    L.off_cursor = o;
+    o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.off_entries = o;
+    L.min_bytes = o;
+    return L;
+}
+
+// Pixel centre coordinate for index j of an image side of size W.
+__device__ __forceinline__ float pixel_centre(int j, int W) {
+    return (float)(2 * j + 1) / (float)W - 1.0f;
+}
+
+// Full evaluation of one (pixel, face) pair, mirroring the conventions
+// operation by operation. `want_dist` forces the distance even when the
+// pixel is inside (needed for the dists output).
+struct PairState {
+    float b0, b1, b2;      // raw barycentrics
+    bool inside;
+    float d2;              // squared distance to the nearest edge (if computed)
+    int argmin;            // nearest edge (first minimum)
+    float t, rx, ry;       // its clamp parameter and residual
+    float c0, c1, c2, invS;
+    float bh0, bh1, bh2;   // clipped, renormalised barycentrics
+    float z;               // depth at the pixel
+    bool cand;             // included and z > 0
+};
+
+__device__ __forceinline__ void edge_distance(float px, float py, float ax, float ay, float bx, float by,
+                                              float il, float& d, float& t, float& rx, float& ry) {
+    float ux = bx - ax;
+    float uy = by - ay;
+    float qx = px - ax;
+    float qy = py - ay;
+    t = (qx * ux + qy * uy) * il;
+    t = t < 0.0f ? 0.0f : t;
+    t = t > 1.0f ? 1.0f : t;
+    rx = qx - t * ux;
+    ry = qy - t * uy;
+    d = rx * rx + ry * ry;
+}
+
+__device__ __forceinline__ void eval_pair(const FaceRec& r, float px, float py, float blur, bool want_dist,
+                                          PairState& s) {
+    float dx0 = r.x0 - px, dy0 = r.y0 - py;
+    float dx1 = r.x1 - px, dy1 = r.y1 - py;
+    float dx2 = r.x2 - px, dy2 = r.y2 - py;
+    float w0 = dx1 * dy2 - dy1 * dx2;
+    float w1 = dx2 * dy0 - dy2 * dx0;
+    float w2 = dx0 * dy1 - dy0 * dx1;
+    s.b0 = w0 * r.invA;
+    s.b1 = w1 * r.invA;
+    s.b2 = w2 * r.invA;
+    bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    s.inside = in_box && (s.b0 > 0.0f) && (s.b1 > 0.0f) && (s.b2 > 0.0f);
+    s.d2 = 0.0f;
+    s.argmin = 0;
+    s.t = s.rx = s.ry = 0.0f;
+    bool included = s.inside;
+    if (want_dist || !s.inside) {
+        float d0, t0, rx0, ry0, d1, t1, rx1, ry1, d2e, t2, rx2, ry2;
+        edge_distance(px, py, r.x0, r.y0, r.x1, r.y1, r.il0, d0, t0, rx0, ry0);
+        edge_distance(px, py, r.x1, r.y1, r.x2, r.y2, r.il1, d1, t1, rx1, ry1);
+        edge_distance(px, py, r.x2, r.y2, r.x0, r.y0, r.il2, d2e, t2, rx2, ry2);
+        s.d2 = d0; s.argmin = 0; s.t = t0; s.rx = rx0; s.ry = ry0;
+        if (d1 < s.d2) { s.d2 = d1; s.argmin = 1; s.t = t1; s.rx = rx1; s.ry = ry1; }
+        if (d2e < s.d2) { s.d2 = d2e; s.argmin = 2; s.t = t2; s.rx = rx2; s.ry = ry2; }
+        included = s.inside || (s.d2 < blur);
+    }
+    s.cand = false;
+    if (!included) return;
+    float c0 = s.b0 < 0.0f ? 0.0f : s.b0;
+    float c1 = s.b1 < 0.0f ? 0.0f : s.b1;
+    float c2 = s.b2 < 0.0f ? 0.0f : s.b2;
+    c0 = c0 > 1.0f ? 1.0f : c0;
+    c1 = c1 > 1.0f ? 1.0f : c1;
+    c2 = c2 > 1.0f ? 1.0f : c2;
+    s.c0 = c0; s.c1 = c1; s.c2 = c2;
+    float S = (c0 + c1) + c2;
+    s.invS = 1.0f / S;
+    s.bh0 = c0 * s.invS;
+    s.bh1 = c1 * s.invS;
+    s.bh2 = c2 * s.invS;
+    s.z = (s.bh0 * r.z0 + s.bh1 * r.z1) + s.bh2 * r.z2;
+    s.cand = s.z > 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// host-side launch helpers implemented in the .hip files
+// ---------------------------------------------------------------------------
+enum KernelId : int32_t {
+    kKZeroFwd = 0,
+    kKFaceSetup,
+    kKBinScan,
+    kKBinFill,
+    kKFineRaster,
+    kKZeroGrad,
+    kKBackward,
+    kKernelCount
+};
+
+struct FwdArgs {
+    const float* verts; int64_t V;
+    const int64_t* faces; int64_t F;
+    const int64_t* off; int64_t N;
+    int32_t H, W, K;
+    float blur;
+    int64_t* pix_to_face; float* zbuf; float* bary; float* dists;
+    char* ws; size_t ws_bytes;
+    FwdLayout L;
+    int64_t capacity;
+    hipStream_t stream;
+};
+
+struct BwdArgs {
+    const float* verts; int64_t V;
+    const int64_t* faces; int64_t F;
+    const int64_t* off; int64_t N;
+    int32_t H, W, K;
+    const int64_t* pix_to_face;
+    const float* gz; const float* gb; const float* gd;
+    float* grad_verts;
+    hipStream_t stream;
+};
+
+// Launch wrappers with optional event timing; return hipSuccess or the error.
+hipError_t launch_forward(const FwdArgs& a);
+hipError_t launch_backward(const BwdArgs& a);
+
+// Timing hooks (api.hip).
+void timing_begin(KernelId id, hipStream_t s);
+void timing_end(KernelId id, hipStream_t s);
+
+}  // namespace dmr

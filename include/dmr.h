@@ -1,0 +1,169 @@
+/*
+ * dmr.h - C ABI of the MI355X (gfx950) K-nearest-face mesh rasterizer.
+ *
+ * The operation is the face-selection stage of the two-stage rasterizer of
+ * "Accelerating 3D Deep Learning with PyTorch3D": for every pixel, select the
+ * faces that influence it and keep the K nearest (gptget.net summary,
+ * "Methodology": stage one selects the faces affecting each pixel; nubint.ai
+ * review, "Proposed method": per-pixel K nearest faces), over a batch of
+ * meshes of different sizes (rocketrecap summary, "1:00 Heterogeneous
+ * Batching"), with per-pixel intermediates returned so that shading can be
+ * composed on top and differentiated (nubint.ai review, "Proposed method";
+ * rocketrecap summary, "3:52 Differentiable Renderer").
+ *
+ * Conventions (the pages fix none of them; these are the library's):
+ *   pixel (i, j) of an H x W image has its centre at
+ *       x = fl(fl((2j+1)/W) - 1),  y = fl(fl((2i+1)/H) - 1)   (binary32, no flip);
+ *   a face is a candidate for a pixel when the centre is strictly inside it
+ *   (all barycentrics > 0, centre in the face's closed bounding box) or its
+ *   squared 2D distance to the face's edges is below blur_radius, it is not
+ *   degenerate (doubled area A != 0) and its depth z at the pixel, from
+ *   barycentrics clipped to [0,1] and renormalised, is > 0;
+ *   each pixel keeps its K candidates of smallest (z, global face index);
+ *   all decisions and values are binary32, evaluated in one fixed operation
+ *   order with no fused multiply-add, so results are reproducible bit for bit.
+ *
+ * Memory: every pointer argument is a device pointer on the device the
+ * stream belongs to (the default device for the null stream); arrays are
+ * row-major, contiguous and must not alias. The library keeps no pointer
+ * after a call returns and owns no device memory. Calls are asynchronous and
+ * ordered on `stream`; results are valid once the stream reaches them.
+ * Calls on different streams may run concurrently if they use different
+ * workspaces.
+ *
+ * Errors: every entry point validates its scalar arguments and pointers on
+ * the host before it launches anything and returns a status; no exception
+ * crosses the ABI. Device data (indices, offsets) is not read on the host:
+ * a vertex index outside [0, V) makes its face a non-candidate and sets
+ * DMR_FLAG_BAD_VERTEX_INDEX in the workspace statistics; offsets that are not
+ * non-decreasing from 0 to F give unspecified (but memory-safe) results.
+ * Non-finite vertex coordinates give unspecified outputs.
+ */
+#ifndef DMR_H
+#define DMR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum dmr_status {
+    DMR_SUCCESS = 0,
+    DMR_ERROR_INVALID_VALUE = 1,        /* a size, pointer or scalar argument is invalid */
+    DMR_ERROR_WORKSPACE_TOO_SMALL = 2,  /* below dmr_workspace_min_size() */
+    DMR_ERROR_HIP = 3,                  /* a HIP runtime call failed (launch, event, copy) */
+    DMR_ERROR_UNSUPPORTED = 4           /* K > DMR_MAX_K, or a size beyond the index limits */
+} dmr_status;
+
+#define DMR_MAX_K 64
+#define DMR_MAX_IMAGE_SIDE 32767
+#define DMR_FLAG_BAD_VERTEX_INDEX 0x1u
+
+/*
+ * Forward pass: K nearest faces per pixel.
+ *
+ *   verts      [V,3] float32  x, y in normalised device coordinates, z = view
+ *                             depth; the vertices of all meshes, packed.
+ *   faces      [F,3] int64    vertex indices into verts (global), packed.
+ *   mesh_face_offsets [N+1] int64  mesh n owns faces [off[n], off[n+1]);
+ *                             off[0] = 0, non-decreasing, off[N] = F. Empty
+ *                             meshes are allowed and give all-padding images.
+ *   H, W       image size, 1..DMR_MAX_IMAGE_SIDE.
+ *   K          faces kept per pixel, 1..DMR_MAX_K.
+ *   blur_radius squared NDC distance; finite and >= 0.
+ *   pix_to_face [N,H,W,K] int64  global face index, ascending (z, face); -1 pads.
+ *   zbuf       [N,H,W,K]   float32  depth at the pixel; -1 on padding.
+ *   bary       [N,H,W,K,3] float32  clipped, renormalised barycentrics; -1 pads.
+ *   dists      [N,H,W,K]   float32  signed squared distance to the face's
+ *                                   edges (< 0 inside); -1 on padding.
+ *   workspace  device scratch of workspace_bytes >= dmr_workspace_min_size();
+ *              dmr_workspace_size_hint() gives a size that normally holds the
+ *              per-bin face lists. Results do not depend on the size: bins
+ *              whose list does not fit are rasterised from their mesh's full
+ *              face range instead (exact, slower), and the size that would
+ *              have held every list is recorded (dmr_workspace_stats).
+ * All outputs are fully overwritten, padding included. Returns DMR_SUCCESS
+ * without launching anything when N*H*W == 0.
+ */
+dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                const int64_t* mesh_face_offsets, int64_t N,
+                                int32_t H, int32_t W, int32_t K, float blur_radius,
+                                int64_t* pix_to_face, float* zbuf, float* bary, float* dists,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Backward pass: maps the gradients of zbuf, bary and dists to vertex
+ * positions (rocketrecap summary, "3:52 Differentiable Renderer": gradients
+ * flow from image pixels back to the 3D parameters).
+ *
+ *   verts, faces, mesh_face_offsets, N, H, W, K: as given to the forward pass.
+ *   pix_to_face [N,H,W,K] int64: the forward pass's output for these inputs.
+ *   grad_zbuf [N,H,W,K], grad_bary [N,H,W,K,3], grad_dists [N,H,W,K] float32:
+ *              upstream gradients; any of them may be NULL (= zero). Values on
+ *              padded slots are ignored.
+ *   grad_verts [V,3] float32: overwritten (not accumulated) with dL/dverts.
+ *   workspace  device scratch of >= dmr_bwd_workspace_size() bytes (may be
+ *              NULL when that is 0).
+ * Per-slot contributions are summed with float32 atomics, so the rounding of
+ * grad_verts may differ between runs.
+ */
+dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                const int64_t* mesh_face_offsets, int64_t N,
+                                int32_t H, int32_t W, int32_t K,
+                                const int64_t* pix_to_face,
+                                const float* grad_zbuf, const float* grad_bary, const float* grad_dists,
+                                float* grad_verts,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Smallest forward workspace (bytes) for these sizes: face records and bin
+ * tables, with room for no per-bin face list. 0 on invalid arguments. */
+size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W);
+
+/* Suggested forward workspace (bytes): the minimum plus an estimate of the
+ * per-bin face lists from F, the image size and blur_radius. 0 on invalid
+ * arguments. */
+size_t dmr_workspace_size_hint(int64_t N, int64_t F, int32_t H, int32_t W, int32_t K, float blur_radius);
+
+/* Backward workspace (bytes) for these sizes. */
+size_t dmr_bwd_workspace_size(int64_t N, int64_t F, int64_t V, int32_t H, int32_t W, int32_t K);
+
+/* What the last forward call on `workspace` recorded. Copies the workspace
+ * header to the host and synchronises `stream`. */
+typedef struct dmr_stats {
+    int64_t required_bytes;   /* workspace that holds every bin list */
+    int64_t bin_entries;      /* face entries over all bins */
+    int64_t bin_capacity;     /* entries the given workspace could hold */
+    int64_t bins;             /* number of bins (N * ceil(H/16) * ceil(W/16)) */
+    int64_t overflow_bins;    /* bins rasterised from the full face range */
+    int64_t live_faces;       /* faces that survived culling */
+    uint32_t flags;           /* DMR_FLAG_* */
+    uint32_t reserved;
+} dmr_stats;
+dmr_status dmr_workspace_stats(const void* workspace, dmr_stats* out, hipStream_t stream);
+
+/* Static description of a status code; never NULL. */
+const char* dmr_status_string(dmr_status s);
+
+/*
+ * Optional per-kernel timing for measurement. When enabled, every launch of
+ * kernel `id` (0 .. dmr_kernel_count()-1) is bracketed with HIP events on
+ * the stream it runs on; dmr_kernel_timing() synchronises on the recorded
+ * events and returns the summed duration (ms) and number of launches since
+ * the last reset. Disabled by default; timing is process-wide and not
+ * thread-safe.
+ */
+int32_t dmr_kernel_count(void);
+const char* dmr_kernel_name(int32_t id);
+dmr_status dmr_set_kernel_timing(int32_t enable);
+dmr_status dmr_kernel_timing(int32_t id, double* total_ms, int64_t* launches);
+dmr_status dmr_reset_kernel_timing(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DMR_H */

@@ -1,0 +1,90 @@
+"""Helpers for the GPU tests: move seeded numpy inputs to the device, call the
+C-ABI entry points through the Python binding, bring results back."""
+
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+DEV = torch.device("cuda:0")
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    import differentiable_mesh_rasterization_amd as dmr
+
+    dmr.lib()  # raises if the HIP library is not built: no silent fallback
+    return dmr
+
+
+def to_dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(DEV)
+
+
+class GpuCase:
+    """Device copies of one workload's inputs."""
+
+    def __init__(self, verts, faces, offsets, H, W, K, blur):
+        self.verts = to_dev(np.asarray(verts, np.float32).reshape(-1, 3))
+        self.faces = to_dev(np.asarray(faces, np.int64).reshape(-1, 3))
+        self.offsets = to_dev(np.asarray(offsets, np.int64))
+        self.H, self.W, self.K, self.blur = int(H), int(W), int(K), float(blur)
+        self.N = self.offsets.shape[0] - 1
+
+    @classmethod
+    def from_workload(cls, w):
+        return cls(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur)
+
+    def forward(self, ws_bytes=None, out=None):
+        import differentiable_mesh_rasterization_amd as dmr
+
+        N, H, W, K = self.N, self.H, self.W, self.K
+        if out is None:
+            out = (torch.empty((N, H, W, K), dtype=torch.int64, device=DEV),
+                   torch.empty((N, H, W, K), dtype=torch.float32, device=DEV),
+                   torch.empty((N, H, W, K, 3), dtype=torch.float32, device=DEV),
+                   torch.empty((N, H, W, K), dtype=torch.float32, device=DEV))
+        if ws_bytes is None:
+            ws_bytes = dmr.dmr_workspace_size_hint(N, self.faces.shape[0], H, W, K, self.blur)
+        ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=DEV)
+        dmr.rasterize_meshes_fwd(self.verts, self.faces, self.offsets, H, W, K, self.blur, *out, ws)
+        torch.cuda.synchronize()
+        self.ws = ws
+        return out
+
+    def backward(self, p2f, gz=None, gb=None, gd=None):
+        import differentiable_mesh_rasterization_amd as dmr
+
+        gv = torch.empty_like(self.verts)
+        dmr.rasterize_meshes_bwd(self.verts, self.faces, self.offsets, self.H, self.W, self.K, p2f,
+                                 gz, gb, gd, gv)
+        torch.cuda.synchronize()
+        return gv
+
+    def stats(self):
+        import differentiable_mesh_rasterization_amd as dmr
+
+        return dmr.dmr_workspace_stats(self.ws)
+
+
+def host(out):
+    return tuple(t.cpu().numpy() for t in out)
+
+
+def rows(out, pixel_ids, K):
+    """Selected pixel rows of device outputs, copied to the host."""
+    idx = torch.from_numpy(np.asarray(pixel_ids, np.int64)).to(DEV)
+    res = []
+    for t in out:
+        flat = t.reshape((-1, K) + tuple(t.shape[4:]))
+        res.append(flat.index_select(0, idx).cpu().numpy())
+    return tuple(res)
+
+
+def say(*a):
+    print(*a, flush=True)

@@ -1,0 +1,126 @@
+"""The C-ABI library loads, exports every function include/dmr.h declares, and
+rejects invalid arguments on the host with the documented status before any
+HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dmr.h")
+
+SUCCESS, INVALID, WS_SMALL, HIP, UNSUPPORTED = 0, 1, 2, 3, 4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s+\**([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def dmr():
+    import differentiable_mesh_rasterization_amd as pkg
+
+    if not os.path.exists(pkg.LIB_PATH):
+        from differentiable_mesh_rasterization_amd import build
+
+        build.build()
+    return pkg
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_size_hint", "dmr_status_string"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(dmr):
+    out = subprocess.run(["nm", "-D", "--defined-only", dmr.LIB_PATH], capture_output=True, text=True,
+                         check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    assert set(declared_functions()) == set(dmr.EXPORTED)
+    lib = dmr.lib()
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings(dmr):
+    for s in range(5):
+        assert dmr.status_string(s)
+    assert dmr.status_string(99) == "unknown status"
+
+
+def test_workspace_sizes(dmr):
+    assert dmr.dmr_workspace_min_size(1, 0, 1, 1) >= 256
+    m = dmr.dmr_workspace_min_size(16, 435200, 256, 256)
+    h = dmr.dmr_workspace_size_hint(16, 435200, 256, 256, 10, 1e-4)
+    assert h > m > 435200 * 80
+    assert dmr.dmr_workspace_min_size(-1, 0, 1, 1) == 0
+    assert dmr.dmr_workspace_min_size(1, 0, 0, 1) == 0
+    assert dmr.dmr_workspace_size_hint(1, 10, 8, 8, 1, -1.0) == 0
+    assert dmr.dmr_workspace_size_hint(1, 10, 8, 8, 1, float("nan")) == 0
+    assert dmr.dmr_bwd_workspace_size(1, 10, 30, 8, 8, 1) >= 0
+
+
+def _fwd(lib, **kw):
+    P = ctypes.c_void_p
+    fake = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+    a = dict(verts=fake, V=3, faces=fake, F=1, off=fake, N=1, H=4, W=4, K=1, blur=0.0,
+             p2f=fake, zbuf=fake, bary=fake, dists=fake, ws=fake, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.rasterize_meshes_fwd(a["verts"], a["V"], a["faces"], a["F"], a["off"], a["N"], a["H"], a["W"],
+                                    a["K"], a["blur"], a["p2f"], a["zbuf"], a["bary"], a["dists"], a["ws"],
+                                    a["ws_bytes"], a["stream"])
+
+
+def _bwd(lib, **kw):
+    fake = ctypes.c_void_p(0x1000)
+    a = dict(verts=fake, V=3, faces=fake, F=1, off=fake, N=1, H=4, W=4, K=1, p2f=fake, gz=None, gb=None,
+             gd=None, gv=fake, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return lib.rasterize_meshes_bwd(a["verts"], a["V"], a["faces"], a["F"], a["off"], a["N"], a["H"], a["W"],
+                                    a["K"], a["p2f"], a["gz"], a["gb"], a["gd"], a["gv"], a["ws"], a["ws_bytes"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=-1), INVALID), (dict(F=-1), INVALID), (dict(N=-1), INVALID),
+    (dict(H=0), INVALID), (dict(W=0), INVALID), (dict(K=0), INVALID),
+    (dict(H=40000), UNSUPPORTED), (dict(K=65), UNSUPPORTED),
+    (dict(blur=-1e-3), INVALID), (dict(blur=float("nan")), INVALID), (dict(blur=float("inf")), INVALID),
+    (dict(verts=None), INVALID), (dict(faces=None), INVALID), (dict(off=None), INVALID),
+    (dict(p2f=None), INVALID), (dict(bary=None), INVALID),
+    (dict(N=1 << 40, H=30000, W=30000, K=64), UNSUPPORTED),
+    (dict(F=1 << 31), UNSUPPORTED),
+    (dict(ws=None), WS_SMALL), (dict(ws_bytes=100), WS_SMALL),
+])
+def test_forward_rejects_invalid_arguments(dmr, kw, status):
+    assert _fwd(dmr.lib(), **kw) == status
+
+
+def test_forward_with_nothing_to_draw_is_a_no_op(dmr):
+    # N = 0: no pixels; succeeds without reading any pointer or touching the GPU
+    assert _fwd(dmr.lib(), N=0, off=None, p2f=None, zbuf=None, bary=None, dists=None, ws=None) == SUCCESS
+    assert _fwd(dmr.lib(), N=0, p2f=None, zbuf=None, bary=None, dists=None, ws=None) == SUCCESS
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=-1), INVALID), (dict(H=0), INVALID), (dict(K=0), INVALID), (dict(K=65), UNSUPPORTED),
+    (dict(gv=None), INVALID), (dict(p2f=None), INVALID), (dict(faces=None), INVALID),
+])
+def test_backward_rejects_invalid_arguments(dmr, kw, status):
+    assert _bwd(dmr.lib(), **kw) == status
+
+
+def test_python_binding_fails_loudly_without_library(tmp_path):
+    import differentiable_mesh_rasterization_amd as pkg
+
+    with pytest.raises(RuntimeError, match="not built"):
+        pkg.lib(str(tmp_path / "missing.so"))

@@ -1,0 +1,204 @@
+"""GPU path against the oracle on edge cases: empty meshes and batches, K
+beyond the candidate count, culled and degenerate faces, exact depth ties,
+pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
+a blur radius covering the image, off-screen faces, one face over every bin,
+thousands of faces in one bin, faces using another mesh's vertices, invalid
+vertex indices, and the hand-worked cases."""
+
+import json
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import GpuCase, host, require_gpu, say
+from parity import assert_forward_parity, compare_forward, oracle_excuse
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_cases.json")
+
+
+@pytest.fixture(scope="module")
+def dmr():
+    return require_gpu()
+
+
+def _check(verts, faces, offsets, H, W, K, blur, expect_flags=0):
+    verts = np.asarray(verts, np.float32).reshape(-1, 3)
+    faces = np.asarray(faces, np.int64).reshape(-1, 3)
+    offsets = np.asarray(offsets, np.int64)
+    g = GpuCase(verts, faces, offsets, H, W, K, blur)
+    got = host(g.forward())
+    ref = oracle.rasterize(verts, faces, offsets, H, W, K, blur)
+    rep = compare_forward(ref, got, K, excuse=oracle_excuse(oracle, verts, faces, offsets, H, W, blur))
+    assert_forward_parity(rep, max_excused_frac=0.0)
+    assert g.stats()["flags"] == expect_flags
+    return got, ref
+
+
+def _soup(seed, F, lo=-1.0, hi=1.0, sigma=0.05, zlo=0.5, zhi=3.0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    c = np.stack([rng.uniform(lo, hi, F), rng.uniform(lo, hi, F), rng.uniform(zlo, zhi, F)], 1)
+    v = (c[:, None, :] + rng.normal(0, sigma, (F, 3, 3))).reshape(-1, 3)
+    return v.astype(np.float32), np.arange(3 * F).reshape(F, 3)
+
+
+CASES = {}
+
+
+def case(fn):
+    CASES[fn.__name__] = fn
+    return fn
+
+
+@case
+def all_meshes_empty():
+    return np.zeros((0, 3)), np.zeros((0, 3)), [0, 0, 0, 0], 8, 8, 3, 0.0
+
+
+@case
+def empty_mesh_between():
+    v, f = _soup(1, 40)
+    return v, f, [0, 20, 20, 40], 24, 24, 4, 1e-3
+
+
+@case
+def k_beyond_candidates_k64():
+    v, f = _soup(2, 30, sigma=0.3)
+    return v, f, [0, 30], 20, 20, 64, 1e-3
+
+
+@case
+def all_culled():
+    v, f = _soup(3, 50, zlo=-2.0, zhi=-0.1, sigma=0.02)
+    return v, f, [0, 50], 16, 16, 2, 1e-3
+
+
+@case
+def straddling_depth():
+    v, f = _soup(4, 60, zlo=-0.2, zhi=0.2, sigma=0.3)
+    return v, f, [0, 60], 32, 32, 3, 0.0
+
+
+@case
+def degenerate_mixed():
+    v, f = _soup(5, 30)
+    v = v.reshape(30, 3, 3)
+    v[::3, 2, :2] = 0.5 * (v[::3, 0, :2] + v[::3, 1, :2])  # collinear
+    v[1::5, 1] = v[1::5, 0]  # repeated vertex
+    return v.reshape(-1, 3), f, [0, 30], 32, 32, 2, 1e-2
+
+
+@case
+def coincident_faces():
+    v, f = _soup(6, 10, sigma=0.3)
+    f = np.concatenate([f, f, f[::-1]])
+    return v, f, [0, 30], 24, 24, 5, 1e-3
+
+
+@case
+def shared_edges_through_centres():
+    # a square split along its diagonal; with 8x8 pixels the centres +-k/8
+    # lie exactly on the diagonal x = y
+    v = [[-0.75, -0.75, 1], [0.75, -0.75, 1], [0.75, 0.75, 1], [-0.75, 0.75, 1]]
+    f = [[0, 1, 2], [0, 2, 3]]
+    return v, f, [0, 2], 8, 8, 2, 0.0
+
+
+@case
+def thin_images_h1():
+    v, f = _soup(7, 50, sigma=0.2)
+    return v, f, [0, 50], 1, 37, 3, 1e-3
+
+
+@case
+def thin_images_w1():
+    v, f = _soup(8, 50, sigma=0.2)
+    return v, f, [0, 50], 45, 1, 3, 1e-3
+
+
+@case
+def one_pixel():
+    v, f = _soup(9, 20, sigma=0.5)
+    return v, f, [0, 20], 1, 1, 4, 0.0
+
+
+@case
+def k1_zbuffer():
+    v, f = _soup(10, 200)
+    return v, f, [0, 200], 40, 33, 1, 0.0
+
+
+@case
+def blur_covers_image():
+    v, f = _soup(11, 12, sigma=0.02)
+    return v, f, [0, 12], 12, 12, 16, 8.0
+
+
+@case
+def off_screen_faces():
+    v, f = _soup(12, 60, lo=1.2, hi=3.0)
+    v2, f2 = _soup(13, 20)
+    v = np.concatenate([v, v2])
+    f = np.concatenate([f, f2 + 180])
+    return v, f, [0, 80], 20, 20, 2, 1e-3
+
+
+@case
+def one_face_over_all_bins():
+    v = [[-3, -3, 2], [5, -3, 1], [-3, 5, 3]]
+    v2, f2 = _soup(14, 40)
+    v = np.concatenate([np.asarray(v, np.float32), v2])
+    f = np.concatenate([[[0, 1, 2]], f2 + 3])
+    return v, f, [0, 41], 150, 170, 3, 1e-4
+
+
+@case
+def thousands_in_one_bin():
+    v, f = _soup(15, 5000, lo=-0.95, hi=-0.9, sigma=0.01)
+    return v, f, [0, 5000], 64, 64, 8, 1e-4
+
+
+@case
+def faces_use_other_meshes_vertices():
+    v, f = _soup(16, 40)
+    f = f.copy()
+    f[30:40] = f[0:10]  # mesh 1 reuses mesh 0's vertices
+    return v, f, [0, 20, 40], 16, 16, 3, 1e-3
+
+
+@case
+def large_coordinates():
+    v = [[-50, -40, 2], [60, -10, 1], [0, 70, 3], [-0.5, -0.5, 1], [0.5, -0.4, 1], [0.1, 0.6, 1]]
+    return v, [[0, 1, 2], [3, 4, 5]], [0, 2], 30, 30, 2, 1e-3
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_edge_case(dmr, name):
+    say(f"[gpu] edge case {name}")
+    _check(*CASES[name]())
+
+
+def test_invalid_vertex_index_is_flagged(dmr):
+    v, f = _soup(17, 20)
+    f = f.copy()
+    f[3, 1] = 10_000
+    f[7, 0] = -5
+    say("[gpu] invalid vertex indices")
+    _check(v, f, [0, 20], 16, 16, 2, 1e-3, expect_flags=1)
+
+
+def test_hand_cases_on_gpu(dmr):
+    with open(GOLDEN) as fh:
+        data = json.load(fh)
+    import test_oracle_golden as T1
+
+    for c in data["cases"]:
+        say(f"[gpu] hand case {c['name']}")
+        v, f, o = T1._inputs(c)
+        g = GpuCase(v, f, o, c["H"], c["W"], c["K"], c["blur"])
+        got = host(g.forward())
+        for a, b in zip(got, T1._expected(c, np.float32)):
+            assert np.array_equal(a, b), c["name"]
