@@ -35,7 +35,7 @@ def algorithmic_bytes(w, filled_slots, live_faces, grads):
     g = (4 if "zbuf" in grads else 0) + (12 if "bary" in grads else 0) + (4 if "dists" in grads else 0)
     bwd = 8 * slots + g * filled_slots + 24 * w.F + 12 * w.V + 12 * w.V
     fwd_total = 28 * slots + 24 * w.F + 12 * w.V
-    return {"fine_raster": fine, "backward_pixels": bwd, "fwd_total": fwd_total, "bwd_total": bwd}
+    return {"fine_raster": fine, "backward_tiles": bwd, "fwd_total": fwd_total, "bwd_total": bwd}
 
 
 def cpu_baseline(w, grads_np, seconds: float):
@@ -156,7 +156,7 @@ def main():
     kernels = {name: {"avg_us": (ms / n * 1e3) if n else None, "launches": n} for name, (ms, n) in kt.items()}
     roofline = None
     if kt:
-        dominant = max(("fine_raster", "backward_pixels"), key=lambda k: kt[k][0])
+        dominant = max(("fine_raster", "backward_tiles"), key=lambda k: kt[k][0])
         ms, n = kt[dominant]
         avg_s = ms / n * 1e-3
         achieved = alg[dominant] / avg_s / 1e9

@@ -32,7 +32,7 @@ Timing g_timing;
 std::mutex g_timing_mu;
 
 const char* const kKernelNames[kKernelCount] = {
-    "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "fine_raster", "zero_grad", "backward_pixels",
+    "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_tiles",
 };
 
 hipEvent_t take_event() {

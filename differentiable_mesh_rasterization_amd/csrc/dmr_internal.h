@@ -20,6 +20,12 @@ namespace dmr {
 constexpr int kBin = 16;
 constexpr int kBinPixels = kBin * kBin;
 constexpr int kFineThreads = kBinPixels;
+// Faces per setup/fill workgroup.
+constexpr int kSetupThreads = 256;
+// Bin lists up to kSortMax faces are ordered by depth lower bound; each
+// such list has kSortMax / kFineThreads per-round depth bounds.
+constexpr int kSortMax = 4096;
+constexpr int kRoundsPerBin = kSortMax / kFineThreads;
 
 // Per-face record written by the setup pass and read by the fine pass
 // (80 bytes, five 16-byte vectors). A face that can never be a candidate
@@ -54,7 +60,8 @@ static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 // Forward workspace layout; every section starts on a 256-byte boundary.
 struct FwdLayout {
     int64_t bins, nbx, nby;
-    size_t off_records, off_count, off_offset, off_cursor, off_entries;
+    int64_t setup_blocks;
+    size_t off_records, off_count, off_offset, off_cursor, off_perm, off_live, off_roundlb, off_entries;
     size_t min_bytes;
 };
 
@@ -74,6 +81,13 @@ inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W) {
     o = align_up(o + (size_t)(L.bins + 1) * sizeof(int64_t), 256);
     L.off_cursor = o;
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.off_perm = o;
+    o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.setup_blocks = (F + kSetupThreads - 1) / kSetupThreads;
+    L.off_live = o;
+    o = align_up(o + (size_t)L.setup_blocks * sizeof(int32_t), 256);
+    L.off_roundlb = o;
+    o = align_up(o + (size_t)L.bins * kRoundsPerBin * sizeof(float), 256);
     L.off_entries = o;
     L.min_bytes = o;
     return L;
@@ -130,7 +144,9 @@ __device__ __forceinline__ void eval_pair(const FaceRec& r, float px, float py, 
     s.argmin = 0;
     s.t = s.rx = s.ry = 0.0f;
     bool included = s.inside;
-    if (want_dist || !s.inside) {
+    // With blur_radius == 0 the distance test d2 < 0 can never pass, so the
+    // distance is only needed for the dists output.
+    if (want_dist || (!s.inside && blur > 0.0f)) {
         float d0, t0, rx0, ry0, d1, t1, rx1, ry1, d2e, t2, rx2, ry2;
         edge_distance(px, py, r.x0, r.y0, r.x1, r.y1, r.il0, d0, t0, rx0, ry0);
         edge_distance(px, py, r.x1, r.y1, r.x2, r.y2, r.il1, d1, t1, rx1, ry1);
@@ -166,6 +182,7 @@ enum KernelId : int32_t {
     kKFaceSetup,
     kKBinScan,
     kKBinFill,
+    kKBinSort,
     kKFineRaster,
     kKZeroGrad,
     kKBackward,

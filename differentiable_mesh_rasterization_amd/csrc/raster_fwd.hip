@@ -28,25 +28,48 @@ __global__ void zero_i32(int32_t* p, int64_t n) {
 // ---------------------------------------------------------------------------
 // K1: per-face setup, culling and bin counting
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void face_setup_count(
+// Bin counts are privatised in LDS for the faces of the block's "home" mesh
+// (the mesh of its first face; packed faces of one mesh are contiguous, so
+// that is nearly every face): LDS atomics per (face, bin), then one global
+// atomic per non-empty (block, bin). Faces of other meshes, and images with
+// more than kHistBins bins, count with global atomics directly.
+constexpr int kHistBins = 4096;
+
+__device__ __forceinline__ int64_t mesh_of(const int64_t* __restrict__ off, int64_t N, int64_t f) {
+    int64_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+        int64_t mid = (lo + hi) >> 1;
+        if (off[mid + 1] > f) hi = mid; else lo = mid + 1;
+    }
+    return lo;
+}
+
+__global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     const float* __restrict__ verts, int64_t V, const int64_t* __restrict__ faces, int64_t F,
     const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W, float blur,
     int32_t nbx, int32_t nby, FaceRec* __restrict__ recs, int32_t* __restrict__ bin_count,
-    WsHeader* __restrict__ hdr) {
-    int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    int32_t* __restrict__ block_live, WsHeader* __restrict__ hdr) {
+    __shared__ int32_t hist[kHistBins];
+    __shared__ int64_t home_s;
+    __shared__ int32_t live_s;
+    const int per_img = nbx * nby;
+    const bool use_lds = per_img <= kHistBins;
+    const int64_t f = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x;
+    if (threadIdx.x == 0) {
+        home_s = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+        live_s = 0;
+    }
+    if (use_lds)
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) hist[q] = 0;
+    __syncthreads();
+    const int64_t home = home_s;
     bool live = false;
     if (f < F) {
         FaceRec r;
         r.face = -1;
         r.box_lo = 0x7fff7fff;  // empty box: lo > hi
         r.box_hi = 0;
-        // mesh of face f: the n with off[n] <= f < off[n+1]
-        int64_t lo = 0, hi = N - 1;
-        while (lo < hi) {
-            int64_t mid = (lo + hi) >> 1;
-            if (off[mid + 1] > f) hi = mid; else lo = mid + 1;
-        }
-        int64_t n = lo;
+        const int64_t n = mesh_of(off, N, f);
         bool ok = (off[n] <= f) && (f < off[n + 1]);
         int64_t vi0 = faces[3 * f + 0], vi1 = faces[3 * f + 1], vi2 = faces[3 * f + 2];
         bool idx_ok = vi0 >= 0 && vi0 < V && vi1 >= 0 && vi1 < V && vi2 >= 0 && vi2 < V;
@@ -97,39 +120,80 @@ __global__ __launch_bounds__(256) void face_setup_count(
                 r.box_lo = j0 | (i0 << 16);
                 r.box_hi = j1 | (i1 << 16);
                 live = true;
-                int32_t* cnt = bin_count + (int64_t)n * nbx * nby;
+                const bool local = use_lds && n == home;
+                int32_t* cnt = bin_count + n * per_img;
                 for (int by = i0 / kBin; by <= i1 / kBin; ++by)
-                    for (int bx = j0 / kBin; bx <= j1 / kBin; ++bx) atomicAdd(&cnt[by * nbx + bx], 1);
+                    for (int bx = j0 / kBin; bx <= j1 / kBin; ++bx) {
+                        if (local) atomicAdd(&hist[by * nbx + bx], 1);
+                        else atomicAdd(&cnt[by * nbx + bx], 1);
+                    }
             }
         }
         recs[f] = r;
     }
-    // one atomic per wave for the live-face count
+    // live-face count: one LDS atomic per wave, one plain store per block
+    // (the scan kernel adds the per-block counts)
     unsigned long long m = __ballot(live);
-    if ((threadIdx.x & 63) == 0 && m) atomicAdd((unsigned long long*)&hdr->live_faces, (unsigned long long)__popcll(m));
+    if ((threadIdx.x & 63) == 0 && m) atomicAdd(&live_s, (int32_t)__popcll(m));
+    __syncthreads();
+    if (threadIdx.x == 0) block_live[blockIdx.x] = live_s;
+    if (use_lds) {
+        int32_t* cnt = bin_count + home * per_img;
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) {
+            const int32_t c = hist[q];
+            if (c) atomicAdd(&cnt[q], c);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
 // K2: exclusive prefix sum of the bin counts (one workgroup), header stats,
-// cursor reset
+// cursor reset, and the order in which the fine pass visits the bins:
+// heaviest first (counting sort on floor(log2(count)) buckets), so that the
+// longest workgroups start early and do not form the kernel's tail.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
+constexpr int kOrderBuckets = 33;
+
+__device__ __forceinline__ int order_bucket(int32_t c) {
+    // descending: bucket 0 holds the largest counts, bucket 32 the empty bins
+    return c <= 0 ? 32 : __clz(c);
+}
 
 __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restrict__ count,
                                                          int64_t* __restrict__ offset,
-                                                         int32_t* __restrict__ cursor, int64_t bins,
-                                                         int64_t capacity, size_t base_bytes,
+                                                         int32_t* __restrict__ cursor,
+                                                         int32_t* __restrict__ perm, int64_t bins,
+                                                         const int32_t* __restrict__ block_live,
+                                                         int64_t nblocks, int64_t capacity, size_t base_bytes,
                                                          WsHeader* __restrict__ hdr) {
     __shared__ int64_t part[kScanThreads];
     __shared__ int64_t ovf[kScanThreads];
+    __shared__ int64_t live_sum;
+    __shared__ int32_t bucket_n[kOrderBuckets];
+    __shared__ int32_t bucket_at[kOrderBuckets];
     const int t = threadIdx.x;
+    if (t < kOrderBuckets) bucket_n[t] = 0;
+    if (t == 0) live_sum = 0;
     const int64_t per = (bins + kScanThreads - 1) / kScanThreads;
     const int64_t b0 = t * per;
     const int64_t b1 = min(bins, b0 + per);
     int64_t s = 0;
-    for (int64_t b = b0; b < b1; ++b) s += count[b];
+    __syncthreads();
+    for (int64_t b = b0; b < b1; ++b) {
+        const int32_t c = count[b];
+        s += c;
+        atomicAdd(&bucket_n[order_bucket(c)], 1);
+    }
     part[t] = s;
     __syncthreads();
+    if (t == 0) {
+        int32_t run = 0;
+        for (int q = 0; q < kOrderBuckets; ++q) {
+            bucket_at[q] = run;
+            run += bucket_n[q];
+        }
+    }
     // Hillis-Steele inclusive scan over the per-thread sums
     for (int d = 1; d < kScanThreads; d <<= 1) {
         int64_t v = (t >= d) ? part[t - d] : 0;
@@ -145,11 +209,16 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         if (run + c > capacity) ++over;
         run += c;
         cursor[b] = 0;
+        perm[atomicAdd(&bucket_at[order_bucket(c)], 1)] = (int32_t)b;
     }
     ovf[t] = over;
+    int64_t lv = 0;
+    for (int64_t q = t; q < nblocks; q += kScanThreads) lv += block_live[q];
+    atomicAdd((unsigned long long*)&live_sum, (unsigned long long)lv);
     __syncthreads();
     if (t == 0) {
         int64_t total = part[kScanThreads - 1];
+        hdr->live_faces = live_sum;
         int64_t o = 0;
         for (int q = 0; q < kScanThreads; ++q) o += ovf[q];
         offset[bins] = total;
@@ -164,33 +233,167 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
 // ---------------------------------------------------------------------------
 // K3: bin fill
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void bin_fill(const FaceRec* __restrict__ recs, int64_t F,
-                                                const int64_t* __restrict__ off, int64_t N,
-                                                const int32_t* __restrict__ count,
-                                                const int64_t* __restrict__ offset,
-                                                int32_t* __restrict__ cursor, int32_t* __restrict__ entries,
-                                                int64_t capacity, int32_t nbx, int32_t nby) {
-    int64_t f = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (f >= F) return;
-    const int32_t box_lo = recs[f].box_lo;
-    const int32_t box_hi = recs[f].box_hi;
-    if (recs[f].face < 0) return;
-    int64_t lo = 0, hi = N - 1;
-    while (lo < hi) {
-        int64_t mid = (lo + hi) >> 1;
-        if (off[mid + 1] > f) hi = mid; else lo = mid + 1;
+// Same privatisation as K1: the block counts its home-mesh entries per bin
+// in LDS, reserves each bin's range with one global atomic, then places its
+// faces at LDS-assigned positions inside the reserved ranges. The order of
+// faces inside a bin list does not affect any result.
+__global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceRec* __restrict__ recs, int64_t F,
+                                                          const int64_t* __restrict__ off, int64_t N,
+                                                          const int32_t* __restrict__ count,
+                                                          const int64_t* __restrict__ offset,
+                                                          int32_t* __restrict__ cursor,
+                                                          int32_t* __restrict__ entries, int64_t capacity,
+                                                          int32_t nbx, int32_t nby) {
+    __shared__ int32_t hist[kHistBins];
+    __shared__ int32_t base[kHistBins];
+    __shared__ int64_t home_s;
+    const int per_img = nbx * nby;
+    const bool use_lds = per_img <= kHistBins;
+    const int64_t f = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x;
+    if (threadIdx.x == 0) home_s = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+    if (use_lds)
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) hist[q] = 0;
+    __syncthreads();
+    const int64_t home = home_s;
+    bool live = false;
+    int j0 = 0, i0 = 0, j1 = -1, i1 = -1;
+    int64_t n = 0;
+    if (f < F) {
+        const int32_t box_lo = recs[f].box_lo;
+        const int32_t box_hi = recs[f].box_hi;
+        if (recs[f].face >= 0) {
+            live = true;
+            n = mesh_of(off, N, f);
+            j0 = box_lo & 0xffff; i0 = box_lo >> 16; j1 = box_hi & 0xffff; i1 = box_hi >> 16;
+        }
     }
-    const int64_t binbase = lo * nbx * nby;
-    int j0 = box_lo & 0xffff, i0 = box_lo >> 16, j1 = box_hi & 0xffff, i1 = box_hi >> 16;
+    const bool local = live && use_lds && n == home;
+    if (local)
+        for (int by = i0 / kBin; by <= i1 / kBin; ++by)
+            for (int bx = j0 / kBin; bx <= j1 / kBin; ++bx) atomicAdd(&hist[by * nbx + bx], 1);
+    if (use_lds) {
+        __syncthreads();
+        const int64_t hb = home * per_img;
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) {
+            const int32_t c = hist[q];
+            if (c) base[q] = atomicAdd(&cursor[hb + q], c);
+            hist[q] = 0;
+        }
+        __syncthreads();
+    }
+    if (!live) return;
+    const int64_t binbase = n * per_img;
     for (int by = i0 / kBin; by <= i1 / kBin; ++by)
         for (int bx = j0 / kBin; bx <= j1 / kBin; ++bx) {
-            int64_t b = binbase + by * nbx + bx;
-            int64_t o = offset[b];
-            if (o + count[b] <= capacity) {
-                int32_t pos = atomicAdd(&cursor[b], 1);
-                entries[o + pos] = (int32_t)f;
-            }
+            const int q = by * nbx + bx;
+            const int64_t gb = binbase + q;
+            const int64_t o = offset[gb];
+            int32_t pos;
+            if (local) pos = base[q] + atomicAdd(&hist[q], 1);
+            else pos = atomicAdd(&cursor[gb], 1);
+            if (o + count[gb] <= capacity) entries[o + pos] = (int32_t)f;
         }
+}
+
+// ---------------------------------------------------------------------------
+// K3b: order each bin's list by the faces' smallest vertex depth
+// ---------------------------------------------------------------------------
+// A bucket sort in LDS (256 buckets over the bin's zmin range, O(n)) puts
+// near faces first. The order is approximate inside a bucket, so the exact
+// guarantee the fine pass relies on is stored beside it: for every round of
+// 256 list positions, the smallest zmin over that round and all later ones.
+// A pixel whose last key lies below a round's bound can skip the rest of the
+// list. Lists longer than kSortMax are left as they are (their bound is -inf).
+constexpr int kSortThreads = 256;
+constexpr int kSortBuckets = 256;
+
+__device__ __forceinline__ uint32_t float_order_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float order_bits_float(uint32_t o) {
+    return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceRec* __restrict__ recs,
+                                                         const int32_t* __restrict__ count,
+                                                         const int64_t* __restrict__ offset,
+                                                         const int32_t* __restrict__ perm,
+                                                         int32_t* __restrict__ entries, int64_t capacity,
+                                                         float* __restrict__ round_lb) {
+    __shared__ int32_t ids[kSortMax];
+    __shared__ float zs[kSortMax];
+    __shared__ int32_t sorted_ids[kSortMax];
+    __shared__ int32_t hist[kSortBuckets];
+    __shared__ uint32_t lo_s, hi_s;
+    __shared__ uint32_t rmin[kRoundsPerBin];
+    const int64_t b = perm[blockIdx.x];
+    const int32_t cnt = count[b];
+    const int64_t o = offset[b];
+    const int t = threadIdx.x;
+    float* lb = round_lb + b * kRoundsPerBin;
+    if (cnt == 0 || o + cnt > capacity || cnt > kSortMax) {
+        if (t < kRoundsPerBin) lb[t] = -__builtin_inff();
+        return;
+    }
+    if (t == 0) {
+        lo_s = 0xffffffffu;
+        hi_s = 0u;
+    }
+    if (t < kSortBuckets) hist[t] = 0;
+    if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
+    __syncthreads();
+    uint32_t mylo = 0xffffffffu, myhi = 0u;
+    for (int q = t; q < cnt; q += kSortThreads) {
+        const int32_t f = entries[o + q];
+        const FaceRec& r = recs[f];
+        const float zmin = fminf(r.z0, fminf(r.z1, r.z2));
+        ids[q] = f;
+        zs[q] = zmin;
+        const uint32_t ob = float_order_bits(zmin);
+        mylo = min(mylo, ob);
+        myhi = max(myhi, ob);
+    }
+    atomicMin(&lo_s, mylo);
+    atomicMax(&hi_s, myhi);
+    __syncthreads();
+    const float lo = order_bits_float(lo_s), hi = order_bits_float(hi_s);
+    const float scale = (hi > lo) ? (float)kSortBuckets / (hi - lo) : 0.0f;
+    for (int q = t; q < cnt; q += kSortThreads) {
+        int k = (int)((zs[q] - lo) * scale);
+        k = k < 0 ? 0 : (k >= kSortBuckets ? kSortBuckets - 1 : k);
+        atomicAdd(&hist[k], 1);
+    }
+    __syncthreads();
+    if (t == 0) {
+        int32_t run = 0;
+        for (int k = 0; k < kSortBuckets; ++k) {
+            const int32_t c = hist[k];
+            hist[k] = run;
+            run += c;
+        }
+    }
+    __syncthreads();
+    for (int q = t; q < cnt; q += kSortThreads) {
+        int k = (int)((zs[q] - lo) * scale);
+        k = k < 0 ? 0 : (k >= kSortBuckets ? kSortBuckets - 1 : k);
+        const int pos = atomicAdd(&hist[k], 1);
+        sorted_ids[pos] = q;
+    }
+    __syncthreads();
+    for (int q = t; q < cnt; q += kSortThreads) {
+        const int src = sorted_ids[q];
+        entries[o + q] = ids[src];
+        atomicMin(&rmin[q / kFineThreads], float_order_bits(zs[src]));
+    }
+    __syncthreads();
+    if (t == 0) {
+        uint32_t run = 0xffffffffu;
+        for (int r = kRoundsPerBin - 1; r >= 0; --r) {
+            run = min(run, rmin[r]);
+            lb[r] = (run == 0xffffffffu) ? __builtin_inff() : order_bits_float(run);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -207,48 +410,78 @@ __device__ __forceinline__ void topk_insert(uint64_t (&key)[KMAX], uint64_t k) {
     }
 }
 
-// Writes one output slot: padding for the empty key, else the face's
-// re-evaluated values (the same operations give the same bits as the key's z).
-__device__ __noinline__ void write_slot(const FaceRec* __restrict__ recs, uint64_t kk, float px, float py,
-                                        float blur, int64_t so, int64_t* __restrict__ pix_to_face,
-                                        float* __restrict__ zbuf, float* __restrict__ bary,
-                                        float* __restrict__ dists) {
-    if (kk == ~0ull) {
-        pix_to_face[so] = -1;
-        zbuf[so] = -1.0f;
-        bary[3 * so + 0] = -1.0f;
-        bary[3 * so + 1] = -1.0f;
-        bary[3 * so + 2] = -1.0f;
-        dists[so] = -1.0f;
-        return;
-    }
-    const int32_t face = (int32_t)(kk & 0xffffffffull);
-    PairState s;
-    eval_pair(recs[face], px, py, blur, true, s);
-    pix_to_face[so] = face;
-    zbuf[so] = s.z;
-    bary[3 * so + 0] = s.bh0;
-    bary[3 * so + 1] = s.bh1;
-    bary[3 * so + 2] = s.bh2;
-    dists[so] = s.inside ? -s.d2 : s.d2;
+// Candidate test of one (pixel, face) pair against the current last key,
+// with the binary32 operations of the conventions in their fixed order. The
+// depth (and so the key) is formed before the distance: a pair whose key
+// cannot enter the list is dropped without its three edge distances. The
+// result equals testing inclusion first.
+__device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float py, float blur, uint64_t last,
+                                              uint64_t& kk) {
+    const float dx0 = r.x0 - px, dy0 = r.y0 - py;
+    const float dx1 = r.x1 - px, dy1 = r.y1 - py;
+    const float dx2 = r.x2 - px, dy2 = r.y2 - py;
+    const float w0 = dx1 * dy2 - dy1 * dx2;
+    const float w1 = dx2 * dy0 - dy2 * dx0;
+    const float w2 = dx0 * dy1 - dy0 * dx1;
+    const float b0 = w0 * r.invA, b1 = w1 * r.invA, b2 = w2 * r.invA;
+    const bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    const bool inside = in_box && (b0 > 0.0f) && (b1 > 0.0f) && (b2 > 0.0f);
+    if (!inside && !(blur > 0.0f)) return false;
+    float c0 = b0 < 0.0f ? 0.0f : b0;
+    float c1 = b1 < 0.0f ? 0.0f : b1;
+    float c2 = b2 < 0.0f ? 0.0f : b2;
+    c0 = c0 > 1.0f ? 1.0f : c0;
+    c1 = c1 > 1.0f ? 1.0f : c1;
+    c2 = c2 > 1.0f ? 1.0f : c2;
+    const float S = (c0 + c1) + c2;
+    const float invS = 1.0f / S;
+    const float z = ((c0 * invS) * r.z0 + (c1 * invS) * r.z1) + (c2 * invS) * r.z2;
+    if (!(z > 0.0f)) return false;
+    kk = ((uint64_t)__float_as_uint(z) << 32) | (uint32_t)r.face;
+    if (!(kk < last)) return false;
+    if (inside) return true;
+    float d0, d1, d2, t, rx, ry;
+    edge_distance(px, py, r.x0, r.y0, r.x1, r.y1, r.il0, d0, t, rx, ry);
+    edge_distance(px, py, r.x1, r.y1, r.x2, r.y2, r.il1, d1, t, rx, ry);
+    edge_distance(px, py, r.x2, r.y2, r.x0, r.y0, r.il2, d2, t, rx, ry);
+    float d = d0;
+    d = d1 < d ? d1 : d;
+    d = d2 < d ? d2 : d;
+    return d < blur;
 }
 
+// One workgroup per bin (visited heaviest first), one thread per pixel.
+// Each round stages up to 256 of the bin's faces in LDS (one per thread).
+// Every wave then describes the pixel boxes of its 64 faces with ballots:
+// colmask[c] has bit u set when face slot u's box covers bin column c, and
+// rowmask[r] likewise for bin row r. A pixel's candidate faces in the round
+// are colmask[its column] & rowmask[its row], so each thread evaluates only
+// the faces whose box contains its pixel. With a depth-sorted list a pixel
+// stops at the first face whose depth lower bound exceeds its last key, and
+// the workgroup stops when all its pixels have.
+// The K output slots of each bin row are then written slot-linearly (lane
+// q writes slot q of the row's contiguous 16*K-slot run) after the keys are
+// exchanged through LDS, so that stores are contiguous across lanes.
 template <int KMAX>
 __global__ __launch_bounds__(kFineThreads) void fine_raster(
     const FaceRec* __restrict__ recs, int64_t F, const int64_t* __restrict__ off,
-    const int32_t* __restrict__ count, const int64_t* __restrict__ offset,
-    const int32_t* __restrict__ entries, int64_t capacity, int32_t H, int32_t W, int32_t K, float blur,
-    int32_t nbx, int32_t nby, int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf,
-    float* __restrict__ bary, float* __restrict__ dists) {
+    const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const int32_t* __restrict__ perm,
+    const int32_t* __restrict__ entries, const float* __restrict__ round_lb, int64_t capacity, int32_t H,
+    int32_t W, int32_t K, float blur, int32_t nbx, int32_t nby, int64_t* __restrict__ pix_to_face,
+    float* __restrict__ zbuf, float* __restrict__ bary, float* __restrict__ dists) {
     __shared__ FaceRec srec[kFineThreads];
-    const int64_t b = blockIdx.x;
+    __shared__ uint64_t colmask[kBin][kFineThreads / 64];
+    __shared__ uint64_t rowmask[kBin][kFineThreads / 64];
+    const int64_t b = perm[blockIdx.x];
     const int64_t per_img = (int64_t)nbx * nby;
     const int64_t n = b / per_img;
     const int rem = (int)(b - n * per_img);
     const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
     const int t = threadIdx.x;
-    const int i = by * kBin + t / kBin;
-    const int j = bx * kBin + (t % kBin);
+    const int lane = t & 63, wave = t >> 6;
+    const int il = t / kBin, jl = t % kBin;
+    const int i = by * kBin + il;
+    const int j = bx * kBin + jl;
     const bool valid = (i < H) && (j < W);
     const float px = pixel_centre(j, W);
     const float py = pixel_centre(i, H);
@@ -260,48 +493,125 @@ __global__ __launch_bounds__(kFineThreads) void fine_raster(
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
     const bool list_mode = (o + cnt <= capacity);
+    const bool sorted = list_mode && cnt <= kSortMax;
+    const float* lb = round_lb + b * kRoundsPerBin;
     int64_t f0 = off[n], f1 = off[n + 1];
     f0 = f0 < 0 ? 0 : f0;
     f1 = f1 > F ? F : f1;
     const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
+    bool done = !valid;
 
     for (int64_t base = 0; base < total; base += kFineThreads) {
+        // Every face from this round on has zmin >= lb[round]; a pixel whose
+        // last key is below that bound (with the rounding margin of the
+        // depth interpolation) is finished.
+        if (sorted && !done) {
+            const float zl = lb[base / kFineThreads] * (1.0f - 0x1.0p-19f) - 1e-30f;
+            if (zl > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) done = true;
+        }
+        if (__syncthreads_count(!done) == 0) break;
         int64_t q = base + t;
+        bool live = false;
+        int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
         if (q < total) {
             int64_t fid = list_mode ? (int64_t)entries[o + q] : f0 + q;
-            srec[t] = recs[fid];
+            FaceRec r = recs[fid];
+            srec[t] = r;
+            if (r.face >= 0) {
+                c0 = max((r.box_lo & 0xffff) - bx * kBin, 0);
+                c1 = min((r.box_hi & 0xffff) - bx * kBin, kBin - 1);
+                r0 = max((r.box_lo >> 16) - by * kBin, 0);
+                r1 = min((r.box_hi >> 16) - by * kBin, kBin - 1);
+                live = (c0 <= c1) && (r0 <= r1);
+            }
+        }
+#pragma unroll
+        for (int c = 0; c < kBin; ++c) {
+            uint64_t mc = __ballot(live && c0 <= c && c <= c1);
+            uint64_t mr = __ballot(live && r0 <= c && c <= r1);
+            if (lane == 0) {
+                colmask[c][wave] = mc;
+                rowmask[c][wave] = mr;
+            }
         }
         __syncthreads();
-        const int m = (int)min((int64_t)kFineThreads, total - base);
-        if (valid) {
-            for (int u = 0; u < m; ++u) {
-                const int32_t face = srec[u].face;
-                const int32_t lo = srec[u].box_lo, hi = srec[u].box_hi;
-                if (face < 0) continue;
-                if (j < (lo & 0xffff) || j > (hi & 0xffff) || i < (lo >> 16) || i > (hi >> 16)) continue;
-                PairState s;
-                eval_pair(srec[u], px, py, blur, false, s);
-                if (!s.cand) continue;
-                uint64_t kk = ((uint64_t)__float_as_uint(s.z) << 32) | (uint32_t)face;
-                if (kk < key[KMAX - 1]) topk_insert<KMAX>(key, kk);
+        if (!done) {
+#pragma unroll 1
+            for (int w = 0; w < kFineThreads / 64; ++w) {
+                uint64_t m = colmask[jl][w] & rowmask[il][w];
+                while (m) {
+                    const int u = w * 64 + __builtin_ctzll(m);
+                    m &= m - 1;
+                    const FaceRec& r = srec[u];
+                    // Depth lower bound: z at any pixel is at least
+                    // min(z0, z1, z2) up to a few roundings, so a face whose
+                    // bound exceeds the last key cannot enter the list.
+                    const float zmin = fminf(r.z0, fminf(r.z1, r.z2));
+                    const float zlo = zmin * (1.0f - 0x1.0p-19f) - 1e-30f;
+                    if (zlo > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) continue;
+                    uint64_t kk;
+                    if (candidate_key(r, px, py, blur, key[KMAX - 1], kk)) topk_insert<KMAX>(key, kk);
+                }
             }
         }
         __syncthreads();
     }
-    if (!valid) return;
-    const int64_t pix = ((int64_t)n * H + i) * W + j;
-    const int64_t sbase = pix * K;
+    __syncthreads();
+
+    // ---- output: exchange keys through LDS (reusing srec), then write each
+    // bin row's 16*K slots with consecutive lanes on consecutive slots
+    uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
+    constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
+    const int rows_per_pass = max(1, min(kBin, kBufKeys / (kBin * K)));
+    for (int r0 = 0; r0 < kBin; r0 += rows_per_pass) {
+        const int r1 = min(kBin, r0 + rows_per_pass);
+        if (il >= r0 && il < r1) {
+            uint64_t* dst = kbuf + ((il - r0) * kBin + jl) * K;
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) {
-        if (q < K) write_slot(recs, key[q], px, py, blur, sbase + q, pix_to_face, zbuf, bary, dists);
+            for (int q = 0; q < KMAX; ++q)
+                if (q < K) dst[q] = key[q];
+        }
+        __syncthreads();
+        const int row_slots = kBin * K;
+        const int npass = (r1 - r0) * row_slots;
+        for (int e = t; e < npass; e += kFineThreads) {
+            const int rr = e / row_slots;
+            const int within = e - rr * row_slots;
+            const int jj = within / K;
+            const int gi = by * kBin + r0 + rr;
+            const int gj = bx * kBin + jj;
+            if (gi >= H || gj >= W) continue;
+            const int64_t so = (((int64_t)n * H + gi) * W + bx * kBin) * K + within;
+            const uint64_t kk = kbuf[e];
+            if (kk == ~0ull) {
+                pix_to_face[so] = -1;
+                zbuf[so] = -1.0f;
+                bary[3 * so + 0] = -1.0f;
+                bary[3 * so + 1] = -1.0f;
+                bary[3 * so + 2] = -1.0f;
+                dists[so] = -1.0f;
+            } else {
+                const int32_t face = (int32_t)(kk & 0xffffffffull);
+                PairState s;
+                eval_pair(recs[face], pixel_centre(gj, W), pixel_centre(gi, H), blur, true, s);
+                pix_to_face[so] = face;
+                zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
+                bary[3 * so + 0] = s.bh0;
+                bary[3 * so + 1] = s.bh1;
+                bary[3 * so + 2] = s.bh2;
+                dists[so] = s.inside ? -s.d2 : s.d2;
+            }
+        }
+        __syncthreads();
     }
 }
+
 template <int KMAX>
 static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const int32_t* count,
-                        const int64_t* offset, const int32_t* entries) {
+                        const int64_t* offset, const int32_t* perm, const int32_t* entries, const float* round_lb) {
     fine_raster<KMAX><<<grid, kFineThreads, 0, a.stream>>>(
-        recs, a.F, a.off, count, offset, entries, a.capacity, a.H, a.W, a.K, a.blur, (int32_t)a.L.nbx,
-        (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
+        recs, a.F, a.off, count, offset, perm, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
+        (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
 }
 
 hipError_t launch_forward(const FwdArgs& a) {
@@ -311,6 +621,9 @@ hipError_t launch_forward(const FwdArgs& a) {
     int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
     int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + a.L.off_cursor);
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + a.L.off_perm);
+    int32_t* block_live = reinterpret_cast<int32_t*>(ws + a.L.off_live);
+    float* round_lb = reinterpret_cast<float*>(ws + a.L.off_roundlb);
     int32_t* entries = reinterpret_cast<int32_t*>(ws + a.L.off_entries);
 
     // header + bin counts to zero (header words are int32-sized multiples)
@@ -322,32 +635,39 @@ hipError_t launch_forward(const FwdArgs& a) {
     }
     if (a.F > 0) {
         timing_begin(kKFaceSetup, a.stream);
-        face_setup_count<<<(unsigned)((a.F + 255) / 256), 256, 0, a.stream>>>(
+        face_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
             a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, (int32_t)a.L.nbx, (int32_t)a.L.nby, recs,
-            count, hdr);
+            count, block_live, hdr);
         timing_end(kKFaceSetup, a.stream);
     }
     timing_begin(kKBinScan, a.stream);
-    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, a.L.bins, a.capacity, a.L.min_bytes, hdr);
+    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, a.L.bins, block_live,
+                                                 a.F > 0 ? a.L.setup_blocks : 0, a.capacity, a.L.min_bytes, hdr);
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {
         timing_begin(kKBinFill, a.stream);
-        bin_fill<<<(unsigned)((a.F + 255) / 256), 256, 0, a.stream>>>(recs, a.F, a.off, a.N, count, offset, cursor,
+        bin_fill<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(recs, a.F, a.off, a.N, count, offset, cursor,
                                                                       entries, a.capacity, (int32_t)a.L.nbx,
                                                                       (int32_t)a.L.nby);
         timing_end(kKBinFill, a.stream);
     }
+    if (a.F > 0) {
+        timing_begin(kKBinSort, a.stream);
+        bin_sort<<<(unsigned)a.L.bins, kSortThreads, 0, a.stream>>>(recs, count, offset, perm, entries, a.capacity,
+                                                                     round_lb);
+        timing_end(kKBinSort, a.stream);
+    }
     dim3 grid((unsigned)a.L.bins);
     timing_begin(kKFineRaster, a.stream);
-    if (a.K <= 1) launch_fine<1>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 2) launch_fine<2>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 4) launch_fine<4>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 8) launch_fine<8>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 10) launch_fine<10>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 16) launch_fine<16>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 32) launch_fine<32>(a, grid, recs, count, offset, entries);
-    else if (a.K <= 50) launch_fine<50>(a, grid, recs, count, offset, entries);
-    else launch_fine<64>(a, grid, recs, count, offset, entries);
+    if (a.K <= 1) launch_fine<1>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 2) launch_fine<2>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 4) launch_fine<4>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 8) launch_fine<8>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 10) launch_fine<10>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 16) launch_fine<16>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 32) launch_fine<32>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else if (a.K <= 50) launch_fine<50>(a, grid, recs, count, offset, perm, entries, round_lb);
+    else launch_fine<64>(a, grid, recs, count, offset, perm, entries, round_lb);
     timing_end(kKFineRaster, a.stream);
     return hipGetLastError();
 }
