@@ -22,11 +22,12 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libdmr.so")
 
 DMR_MAX_K = 64
+DMR_BWD_REUSE_FORWARD_WORKSPACE = 0x1
 STATUS = {0: "DMR_SUCCESS", 1: "DMR_ERROR_INVALID_VALUE", 2: "DMR_ERROR_WORKSPACE_TOO_SMALL",
           3: "DMR_ERROR_HIP", 4: "DMR_ERROR_UNSUPPORTED"}
 EXPORTED = [
     "rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
-    "dmr_bwd_workspace_size", "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
+    "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_kernel_timing", "dmr_reset_kernel_timing",
 ]
 
@@ -61,13 +62,12 @@ def lib(path: Optional[str] = None):
     L.rasterize_meshes_fwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
                                        P, P, P, P, P, SZ, P]
     L.rasterize_meshes_bwd.restype = ctypes.c_int
-    L.rasterize_meshes_bwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, P, P, P, P, P, P, SZ, P]
+    L.rasterize_meshes_bwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P, SZ,
+                                       ctypes.c_uint32, P]
     L.dmr_workspace_min_size.restype = SZ
     L.dmr_workspace_min_size.argtypes = [I64, I64, I32, I32]
     L.dmr_workspace_size_hint.restype = SZ
     L.dmr_workspace_size_hint.argtypes = [I64, I64, I32, I32, I32, ctypes.c_float]
-    L.dmr_bwd_workspace_size.restype = SZ
-    L.dmr_bwd_workspace_size.argtypes = [I64, I64, I64, I32, I32, I32]
     L.dmr_workspace_stats.restype = ctypes.c_int
     L.dmr_workspace_stats.argtypes = [P, ctypes.POINTER(dmr_stats), P]
     L.dmr_status_string.restype = ctypes.c_char_p
@@ -129,10 +129,6 @@ def dmr_workspace_size_hint(N: int, F: int, H: int, W: int, K: int, blur_radius:
     return int(lib().dmr_workspace_size_hint(N, F, H, W, K, blur_radius))
 
 
-def dmr_bwd_workspace_size(N: int, F: int, V: int, H: int, W: int, K: int) -> int:
-    return int(lib().dmr_bwd_workspace_size(N, F, V, H, W, K))
-
-
 def dmr_workspace_stats(workspace: torch.Tensor) -> dict:
     s = dmr_stats()
     rc = lib().dmr_workspace_stats(_ptr(workspace), ctypes.byref(s), _stream_handle(workspace.device))
@@ -170,11 +166,14 @@ def rasterize_meshes_fwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
 
 
 def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
-                         H: int, W: int, K: int, pix_to_face: torch.Tensor,
+                         H: int, W: int, K: int, blur_radius: float, pix_to_face: torch.Tensor,
                          grad_zbuf: Optional[torch.Tensor], grad_bary: Optional[torch.Tensor],
                          grad_dists: Optional[torch.Tensor], grad_verts: torch.Tensor,
-                         workspace: Optional[torch.Tensor] = None) -> None:
-    """C-ABI backward call on preallocated device tensors (include/dmr.h)."""
+                         workspace: Optional[torch.Tensor] = None, reuse_forward_workspace: bool = False) -> None:
+    """C-ABI backward call on preallocated device tensors (include/dmr.h).
+
+    With reuse_forward_workspace=True, `workspace` must be the forward call's
+    workspace for these same inputs, unmodified since."""
     dev = verts.device
     N = mesh_face_offsets.shape[0] - 1
     shape = (N, H, W, K)
@@ -186,11 +185,13 @@ def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
     _check(grad_bary, "grad_bary", torch.float32, dev, shape + (3,), optional=True)
     _check(grad_dists, "grad_dists", torch.float32, dev, shape, optional=True)
     _check(grad_verts, "grad_verts", torch.float32, dev, tuple(verts.shape))
-    _check(workspace, "workspace", torch.uint8, dev, optional=True)
+    _check(workspace, "workspace", torch.uint8, dev, optional=not reuse_forward_workspace)
+    flags = DMR_BWD_REUSE_FORWARD_WORKSPACE if reuse_forward_workspace else 0
     rc = lib().rasterize_meshes_bwd(
         _ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
-        H, W, K, _ptr(pix_to_face), _ptr(grad_zbuf), _ptr(grad_bary), _ptr(grad_dists), _ptr(grad_verts),
-        _ptr(workspace), 0 if workspace is None else workspace.numel(), _stream_handle(dev))
+        H, W, K, float(blur_radius), _ptr(pix_to_face), _ptr(grad_zbuf), _ptr(grad_bary), _ptr(grad_dists),
+        _ptr(grad_verts), _ptr(workspace), 0 if workspace is None else workspace.numel(), flags,
+        _stream_handle(dev))
     if rc != 0:
         raise DmrError("rasterize_meshes_bwd", rc)
 
@@ -242,24 +243,27 @@ class _RasterizeMeshes(torch.autograd.Function):
     def forward(ctx, verts, faces, offsets, H, W, K, blur_radius):
         N = offsets.shape[0] - 1
         out = _alloc_outputs(N, H, W, K, verts.device)
-        ws = workspace_for(verts.device)
-        buf = ws.ensure(dmr_workspace_size_hint(N, faces.shape[0], H, W, K, blur_radius))
-        rasterize_meshes_fwd(verts, faces, offsets, H, W, K, blur_radius, *out, buf)
-        ctx.save_for_backward(verts, faces, offsets, out[0])
-        ctx.dims = (H, W, K)
+        # Each call owns its workspace: the backward pass reuses its face
+        # records and bin lists, so it must survive until then.
+        ws = torch.empty(dmr_workspace_size_hint(N, faces.shape[0], H, W, K, blur_radius), dtype=torch.uint8,
+                         device=verts.device)
+        rasterize_meshes_fwd(verts, faces, offsets, H, W, K, blur_radius, *out, ws)
+        ctx.save_for_backward(verts, faces, offsets, out[0], ws)
+        ctx.dims = (H, W, K, blur_radius)
         ctx.mark_non_differentiable(out[0])
         return out
 
     @staticmethod
     def backward(ctx, g_p2f, g_zbuf, g_bary, g_dists):
-        verts, faces, offsets, p2f = ctx.saved_tensors
-        H, W, K = ctx.dims
+        verts, faces, offsets, p2f, ws = ctx.saved_tensors
+        H, W, K, blur_radius = ctx.dims
         grad_verts = torch.empty_like(verts)
 
         def c(g):
             return None if g is None else g.contiguous()
 
-        rasterize_meshes_bwd(verts, faces, offsets, H, W, K, p2f, c(g_zbuf), c(g_bary), c(g_dists), grad_verts)
+        rasterize_meshes_bwd(verts, faces, offsets, H, W, K, blur_radius, p2f, c(g_zbuf), c(g_bary), c(g_dists),
+                             grad_verts, ws, reuse_forward_workspace=True)
         return grad_verts, None, None, None, None, None, None
 
 

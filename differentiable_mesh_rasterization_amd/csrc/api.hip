@@ -32,7 +32,7 @@ Timing g_timing;
 std::mutex g_timing_mu;
 
 const char* const kKernelNames[kKernelCount] = {
-    "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_tiles",
+    "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_slots",
 };
 
 hipEvent_t take_event() {
@@ -145,11 +145,6 @@ size_t dmr_workspace_size_hint(int64_t N, int64_t F, int32_t H, int32_t W, int32
     return align_up(base + (size_t)entries * sizeof(int32_t), 256);
 }
 
-size_t dmr_bwd_workspace_size(int64_t N, int64_t F, int64_t V, int32_t H, int32_t W, int32_t K) {
-    (void)N; (void)F; (void)V; (void)H; (void)W; (void)K;
-    return 0;
-}
-
 dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
                                 const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
                                 float blur_radius, int64_t* pix_to_face, float* zbuf, float* bary,
@@ -177,22 +172,31 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
 
 dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
                                 const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
-                                const int64_t* pix_to_face, const float* grad_zbuf, const float* grad_bary,
-                                const float* grad_dists, float* grad_verts, void* workspace,
-                                size_t workspace_bytes, hipStream_t stream) {
+                                float blur_radius, const int64_t* pix_to_face, const float* grad_zbuf,
+                                const float* grad_bary, const float* grad_dists, float* grad_verts, void* workspace,
+                                size_t workspace_bytes, uint32_t flags, hipStream_t stream) {
     int64_t slots = 0;
     dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
     if (st != DMR_SUCCESS) return st;
+    if (!isfinite(blur_radius) || blur_radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
+    if ((flags & ~(uint32_t)DMR_BWD_REUSE_FORWARD_WORKSPACE) != 0) return DMR_ERROR_INVALID_VALUE;
     if (V > 0 && grad_verts == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (slots > 0 && pix_to_face == nullptr) return DMR_ERROR_INVALID_VALUE;
-    if (workspace_bytes < dmr_bwd_workspace_size(N, F, V, H, W, K)) return DMR_ERROR_WORKSPACE_TOO_SMALL;
     if (V == 0) return DMR_SUCCESS;
+    FwdLayout L = fwd_layout(N, F, H, W);
+    if (L.bins > (int64_t)UINT32_MAX) return DMR_ERROR_UNSUPPORTED;
+    const bool reuse = (flags & DMR_BWD_REUSE_FORWARD_WORKSPACE) != 0;
+    if (reuse && slots > 0 && (workspace == nullptr || workspace_bytes < L.min_bytes))
+        return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    int64_t cap = (reuse && slots > 0) ? (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t)) : 0;
+    if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
     BwdArgs a;
     a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
-    a.H = H; a.W = W; a.K = K; a.pix_to_face = pix_to_face;
+    a.H = H; a.W = W; a.K = K; a.blur = blur_radius; a.pix_to_face = pix_to_face;
     a.gz = grad_zbuf; a.gb = grad_bary; a.gd = grad_dists; a.grad_verts = grad_verts;
+    a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes; a.L = L; a.capacity = cap;
+    a.reuse_forward = reuse;
     a.stream = stream;
-    (void)workspace;
     return launch_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
 }
 

@@ -207,13 +207,19 @@ struct BwdArgs {
     const int64_t* faces; int64_t F;
     const int64_t* off; int64_t N;
     int32_t H, W, K;
+    float blur;
     const int64_t* pix_to_face;
     const float* gz; const float* gb; const float* gd;
     float* grad_verts;
+    char* ws; size_t ws_bytes;
+    FwdLayout L;
+    int64_t capacity;
+    bool reuse_forward;
     hipStream_t stream;
 };
 
 // Launch wrappers with optional event timing; return hipSuccess or the error.
+hipError_t launch_binning(const FwdArgs& a, bool sort);
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a);
 

@@ -614,7 +614,7 @@ static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const 
         (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
 }
 
-hipError_t launch_forward(const FwdArgs& a) {
+hipError_t launch_binning(const FwdArgs& a, bool sort) {
     char* ws = a.ws;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
     FaceRec* recs = reinterpret_cast<FaceRec*>(ws + a.L.off_records);
@@ -651,12 +651,25 @@ hipError_t launch_forward(const FwdArgs& a) {
                                                                       (int32_t)a.L.nby);
         timing_end(kKBinFill, a.stream);
     }
-    if (a.F > 0) {
+    if (a.F > 0 && sort) {
         timing_begin(kKBinSort, a.stream);
         bin_sort<<<(unsigned)a.L.bins, kSortThreads, 0, a.stream>>>(recs, count, offset, perm, entries, a.capacity,
                                                                      round_lb);
         timing_end(kKBinSort, a.stream);
     }
+    return hipGetLastError();
+}
+
+hipError_t launch_forward(const FwdArgs& a) {
+    hipError_t err = launch_binning(a, true);
+    if (err != hipSuccess) return err;
+    char* ws = a.ws;
+    FaceRec* recs = reinterpret_cast<FaceRec*>(ws + a.L.off_records);
+    int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
+    int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
+    int32_t* perm = reinterpret_cast<int32_t*>(ws + a.L.off_perm);
+    float* round_lb = reinterpret_cast<float*>(ws + a.L.off_roundlb);
+    int32_t* entries = reinterpret_cast<int32_t*>(ws + a.L.off_entries);
     dim3 grid((unsigned)a.L.bins);
     timing_begin(kKFineRaster, a.stream);
     if (a.K <= 1) launch_fine<1>(a, grid, recs, count, offset, perm, entries, round_lb);

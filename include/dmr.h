@@ -100,24 +100,33 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
  * positions (rocketrecap summary, "3:52 Differentiable Renderer": gradients
  * flow from image pixels back to the 3D parameters).
  *
- *   verts, faces, mesh_face_offsets, N, H, W, K: as given to the forward pass.
- *   pix_to_face [N,H,W,K] int64: the forward pass's output for these inputs.
+ *   verts, faces, mesh_face_offsets, N, H, W, K, blur_radius: as given to the
+ *              forward pass that produced pix_to_face.
+ *   pix_to_face [N,H,W,K] int64: that forward pass's output.
  *   grad_zbuf [N,H,W,K], grad_bary [N,H,W,K,3], grad_dists [N,H,W,K] float32:
  *              upstream gradients; any of them may be NULL (= zero). Values on
  *              padded slots are ignored.
  *   grad_verts [V,3] float32: overwritten (not accumulated) with dL/dverts.
- *   workspace  device scratch of >= dmr_bwd_workspace_size() bytes (may be
- *              NULL when that is 0).
- * Per-slot contributions are summed with float32 atomics, so the rounding of
- * grad_verts may differ between runs.
+ *   workspace, flags
+ *              With flags = DMR_BWD_REUSE_FORWARD_WORKSPACE, `workspace` is the
+ *              forward pass's workspace for these same inputs, unmodified
+ *              since that call (workspace_bytes as given to it); its per-face
+ *              records replace recomputing each face's data from verts and
+ *              faces. The caller guarantees this; it is not checked, and any
+ *              other content gives wrong gradients. With flags = 0 the
+ *              workspace is not used and may be NULL.
+ * Contributions are summed per 16x16 tile and vertex in LDS, then added to
+ * grad_verts with float32 atomics, so the rounding of grad_verts may differ
+ * between runs.
  */
+#define DMR_BWD_REUSE_FORWARD_WORKSPACE 0x1u
 dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
                                 const int64_t* mesh_face_offsets, int64_t N,
-                                int32_t H, int32_t W, int32_t K,
+                                int32_t H, int32_t W, int32_t K, float blur_radius,
                                 const int64_t* pix_to_face,
                                 const float* grad_zbuf, const float* grad_bary, const float* grad_dists,
                                 float* grad_verts,
-                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                void* workspace, size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
 /* Smallest forward workspace (bytes) for these sizes: face records and bin
  * tables, with room for no per-bin face list. 0 on invalid arguments. */
@@ -127,9 +136,6 @@ size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W);
  * per-bin face lists from F, the image size and blur_radius. 0 on invalid
  * arguments. */
 size_t dmr_workspace_size_hint(int64_t N, int64_t F, int32_t H, int32_t W, int32_t K, float blur_radius);
-
-/* Backward workspace (bytes) for these sizes. */
-size_t dmr_bwd_workspace_size(int64_t N, int64_t F, int64_t V, int32_t H, int32_t W, int32_t K);
 
 /* What the last forward call on `workspace` recorded. Copies the workspace
  * header to the host and synchronises `stream`. */

@@ -57,12 +57,15 @@ class GpuCase:
         self.ws = ws
         return out
 
-    def backward(self, p2f, gz=None, gb=None, gd=None):
+    def backward(self, p2f, gz=None, gb=None, gd=None, reuse=True):
+        """Backward pass; with reuse=True it takes the workspace of the last
+        forward() call (same inputs), otherwise none (face data recomputed)."""
         import differentiable_mesh_rasterization_amd as dmr
 
         gv = torch.empty_like(self.verts)
-        dmr.rasterize_meshes_bwd(self.verts, self.faces, self.offsets, self.H, self.W, self.K, p2f,
-                                 gz, gb, gd, gv)
+        ws = self.ws if reuse else None
+        dmr.rasterize_meshes_bwd(self.verts, self.faces, self.offsets, self.H, self.W, self.K, self.blur, p2f,
+                                 gz, gb, gd, gv, ws, reuse_forward_workspace=reuse)
         torch.cuda.synchronize()
         return gv
 

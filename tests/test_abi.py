@@ -66,7 +66,6 @@ def test_workspace_sizes(dmr):
     assert dmr.dmr_workspace_min_size(1, 0, 0, 1) == 0
     assert dmr.dmr_workspace_size_hint(1, 10, 8, 8, 1, -1.0) == 0
     assert dmr.dmr_workspace_size_hint(1, 10, 8, 8, 1, float("nan")) == 0
-    assert dmr.dmr_bwd_workspace_size(1, 10, 30, 8, 8, 1) >= 0
 
 
 def _fwd(lib, **kw):
@@ -82,12 +81,12 @@ def _fwd(lib, **kw):
 
 def _bwd(lib, **kw):
     fake = ctypes.c_void_p(0x1000)
-    a = dict(verts=fake, V=3, faces=fake, F=1, off=fake, N=1, H=4, W=4, K=1, p2f=fake, gz=None, gb=None,
-             gd=None, gv=fake, ws=None, ws_bytes=0, stream=None)
+    a = dict(verts=fake, V=3, faces=fake, F=1, off=fake, N=1, H=4, W=4, K=1, blur=0.0, p2f=fake, gz=None,
+             gb=None, gd=None, gv=fake, ws=fake, ws_bytes=1 << 20, flags=0, stream=None)
     a.update(kw)
     return lib.rasterize_meshes_bwd(a["verts"], a["V"], a["faces"], a["F"], a["off"], a["N"], a["H"], a["W"],
-                                    a["K"], a["p2f"], a["gz"], a["gb"], a["gd"], a["gv"], a["ws"], a["ws_bytes"],
-                                    a["stream"])
+                                    a["K"], a["blur"], a["p2f"], a["gz"], a["gb"], a["gd"], a["gv"], a["ws"],
+                                    a["ws_bytes"], a["flags"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -114,6 +113,8 @@ def test_forward_with_nothing_to_draw_is_a_no_op(dmr):
 @pytest.mark.parametrize("kw,status", [
     (dict(V=-1), INVALID), (dict(H=0), INVALID), (dict(K=0), INVALID), (dict(K=65), UNSUPPORTED),
     (dict(gv=None), INVALID), (dict(p2f=None), INVALID), (dict(faces=None), INVALID),
+    (dict(blur=-1.0), INVALID), (dict(blur=float("nan")), INVALID), (dict(flags=2), INVALID),
+    (dict(ws=None, flags=1), WS_SMALL), (dict(ws_bytes=100, flags=1), WS_SMALL),
 ])
 def test_backward_rejects_invalid_arguments(dmr, kw, status):
     assert _bwd(dmr.lib(), **kw) == status

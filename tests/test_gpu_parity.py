@@ -164,6 +164,37 @@ def test_overflow_path_is_exact(dmr, name):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name", ["small_hetero", "small_soups"])
+def test_backward_rebuild_matches_reuse(dmr, name):
+    """Without the forward's workspace the backward pass recomputes each
+    face's data from verts and faces; the result matches reusing it."""
+    w = make_workload(name)
+    say(f"[gpu] backward without the forward workspace {name}")
+    g = GpuCase.from_workload(w)
+    out = g.forward()
+    gr = upstream_grads(w)
+    args = (out[0], to_dev(gr["zbuf"]), to_dev(gr["bary"]), to_dev(gr["dists"]))
+    a = g.backward(*args, reuse=True).cpu().numpy()
+    b = g.backward(*args, reuse=False).cpu().numpy()
+    assert rel_l2(b, a) <= 1e-6
+
+
+@pytest.mark.parametrize("scale", [1e-6, 1e7])
+def test_backward_gradient_scales(dmr, scale):
+    """Tiny and huge upstream gradients: per-tile sums are fixed point for
+    moderate contributions and fall back to float atomics for large ones;
+    both ends must still match the oracle."""
+    w = make_workload("small_hetero")
+    say(f"[gpu] backward with upstream gradients scaled by {scale}")
+    g = GpuCase.from_workload(w)
+    out = g.forward()
+    gr = {k: (None if a is None else (a * np.float32(scale)).astype(np.float32)) for k, a in upstream_grads(w).items()}
+    gv = g.backward(out[0], to_dev(gr["zbuf"]), to_dev(gr["bary"]), to_dev(gr["dists"])).cpu().numpy()
+    ref = oracle.backward(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur, out[0].cpu().numpy(),
+                          gr["zbuf"], gr["bary"], gr["dists"])
+    assert rel_l2(gv, ref) <= 1e-4, rel_l2(gv, ref)
+
+
 def test_deterministic(dmr):
     w = make_workload("small_soups")
     say("[gpu] determinism")
