@@ -156,7 +156,8 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
     if (slots == 0) return DMR_SUCCESS;
     if (!pix_to_face || !zbuf || !bary || !dists) return DMR_ERROR_INVALID_VALUE;
     FwdLayout L = fwd_layout(N, F, H, W);
-    if (L.bins > (int64_t)UINT32_MAX) return DMR_ERROR_UNSUPPORTED;
+    // work items of the fine pass are bin << 3 | part in 32 bits, four per bin at most
+    if (L.bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < L.min_bytes) return DMR_ERROR_WORKSPACE_TOO_SMALL;
     int64_t cap = (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t));
     if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;

@@ -26,6 +26,13 @@ constexpr int kSetupThreads = 256;
 // such list has kSortMax / kFineThreads per-round depth bounds.
 constexpr int kSortMax = 4096;
 constexpr int kRoundsPerBin = kSortMax / kFineThreads;
+// The fine pass takes its work from a queue of items, heaviest first. A bin
+// with at least kSplitMin faces becomes four items, one per 8x8 quarter,
+// each worked by four lanes per pixel (for K <= kSplitMaxK); any other bin
+// is one item worked by one lane per pixel.
+constexpr int kSplitMin = 1024;
+constexpr int kSplitMaxK = 16;
+constexpr int kItemWhole = 4;   // item code: bin << 3 | quarter (0..3) or kItemWhole
 
 // Per-face record written by the setup pass and read by the fine pass
 // (80 bytes, five 16-byte vectors). A face that can never be a candidate
@@ -53,7 +60,9 @@ struct WsHeader {
     int64_t live_faces;
     uint32_t flags;
     uint32_t reserved;
-    int64_t pad[25];
+    int32_t fine_items;    // work items of the fine pass (written by the scan)
+    int32_t pad32;
+    int64_t pad[24];
 };
 static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 
@@ -61,7 +70,7 @@ static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 struct FwdLayout {
     int64_t bins, nbx, nby;
     int64_t setup_blocks;
-    size_t off_records, off_count, off_offset, off_cursor, off_perm, off_live, off_roundlb, off_entries;
+    size_t off_records, off_count, off_offset, off_cursor, off_perm, off_items, off_live, off_roundlb, off_entries;
     size_t min_bytes;
 };
 
@@ -83,6 +92,8 @@ inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W) {
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
     L.off_perm = o;
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.off_items = o;
+    o = align_up(o + (size_t)L.bins * 4 * sizeof(int32_t), 256);
     L.setup_blocks = (F + kSetupThreads - 1) / kSetupThreads;
     L.off_live = o;
     o = align_up(o + (size_t)L.setup_blocks * sizeof(int32_t), 256);

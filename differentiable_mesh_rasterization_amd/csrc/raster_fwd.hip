@@ -148,22 +148,25 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
 
 // ---------------------------------------------------------------------------
 // K2: exclusive prefix sum of the bin counts (one workgroup), header stats,
-// cursor reset, and the order in which the fine pass visits the bins:
-// heaviest first (counting sort on floor(log2(count)) buckets), so that the
-// longest workgroups start early and do not form the kernel's tail.
+// cursor reset, the order in which the sort visits the bins, and the work
+// items of the fine pass. Both orders put the heaviest work first (counting
+// sort on floor(log2(weight)) buckets), so that long workgroups start early
+// and do not form the kernel's tail. A bin with at least kSplitMin faces
+// (when K allows) gives four quarter items of a quarter of its weight.
 // ---------------------------------------------------------------------------
 constexpr int kScanThreads = 1024;
 constexpr int kOrderBuckets = 33;
 
 __device__ __forceinline__ int order_bucket(int32_t c) {
-    // descending: bucket 0 holds the largest counts, bucket 32 the empty bins
+    // descending: bucket 0 holds the largest weights, bucket 32 the empty bins
     return c <= 0 ? 32 : __clz(c);
 }
 
 __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restrict__ count,
                                                          int64_t* __restrict__ offset,
                                                          int32_t* __restrict__ cursor,
-                                                         int32_t* __restrict__ perm, int64_t bins,
+                                                         int32_t* __restrict__ perm, uint32_t* __restrict__ items,
+                                                         int64_t bins, int32_t allow_split,
                                                          const int32_t* __restrict__ block_live,
                                                          int64_t nblocks, int64_t capacity, size_t base_bytes,
                                                          WsHeader* __restrict__ hdr) {
@@ -172,8 +175,13 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
     __shared__ int64_t live_sum;
     __shared__ int32_t bucket_n[kOrderBuckets];
     __shared__ int32_t bucket_at[kOrderBuckets];
+    __shared__ int32_t item_n[kOrderBuckets];
+    __shared__ int32_t item_at[kOrderBuckets];
     const int t = threadIdx.x;
-    if (t < kOrderBuckets) bucket_n[t] = 0;
+    if (t < kOrderBuckets) {
+        bucket_n[t] = 0;
+        item_n[t] = 0;
+    }
     if (t == 0) live_sum = 0;
     const int64_t per = (bins + kScanThreads - 1) / kScanThreads;
     const int64_t b0 = t * per;
@@ -184,15 +192,20 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         const int32_t c = count[b];
         s += c;
         atomicAdd(&bucket_n[order_bucket(c)], 1);
+        const bool split = allow_split && c >= kSplitMin;
+        atomicAdd(&item_n[order_bucket(split ? c / 4 : c)], split ? 4 : 1);
     }
     part[t] = s;
     __syncthreads();
     if (t == 0) {
-        int32_t run = 0;
+        int32_t run = 0, irun = 0;
         for (int q = 0; q < kOrderBuckets; ++q) {
             bucket_at[q] = run;
             run += bucket_n[q];
+            item_at[q] = irun;
+            irun += item_n[q];
         }
+        hdr->fine_items = irun;
     }
     // Hillis-Steele inclusive scan over the per-thread sums
     for (int d = 1; d < kScanThreads; d <<= 1) {
@@ -210,6 +223,13 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         run += c;
         cursor[b] = 0;
         perm[atomicAdd(&bucket_at[order_bucket(c)], 1)] = (int32_t)b;
+        const uint32_t code = (uint32_t)b << 3;
+        if (allow_split && c >= kSplitMin) {
+            const int at = atomicAdd(&item_at[order_bucket(c / 4)], 4);
+            for (int q = 0; q < 4; ++q) items[at + q] = code | (uint32_t)q;
+        } else {
+            items[atomicAdd(&item_at[order_bucket(c)], 1)] = code | (uint32_t)kItemWhole;
+        }
     }
     ovf[t] = over;
     int64_t lv = 0;
@@ -399,15 +419,34 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceRec* __restri
 // ---------------------------------------------------------------------------
 // K4: fine rasterization with a register top-K
 // ---------------------------------------------------------------------------
+// Insert k into the ascending list key[0..KMAX-1], dropping the largest.
+// Every slot takes its new value from the old list: slot q keeps key[q] when
+// k is not below it, and otherwise takes k or key[q-1], whichever is larger.
 template <int KMAX>
 __device__ __forceinline__ void topk_insert(uint64_t (&key)[KMAX], uint64_t k) {
+    bool lt[KMAX];
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) {
-        uint64_t a = key[q];
-        bool lt = k < a;
-        key[q] = lt ? k : a;
-        k = lt ? a : k;
+    for (int q = 0; q < KMAX; ++q) lt[q] = k < key[q];
+#pragma unroll
+    for (int q = KMAX - 1; q > 0; --q) {
+        const uint64_t from = lt[q - 1] ? key[q - 1] : k;
+        key[q] = lt[q] ? from : key[q];
     }
+    key[0] = lt[0] ? k : key[0];
+}
+
+// Squared distance from the pixel to the segment a->b, given dxa = ax - px,
+// dya = ay - py and the segment vector (ux, uy). The conventions write the
+// clamp parameter with q = p - a = -(dxa, dya); negation is exact in
+// binary32, so t and the residual below equal theirs up to sign, and the
+// squared length is bit-identical.
+__device__ __forceinline__ float edge_dist2(float dxa, float dya, float ux, float uy, float il) {
+    float t = -((dxa * ux + dya * uy) * il);
+    t = t < 0.0f ? 0.0f : t;
+    t = t > 1.0f ? 1.0f : t;
+    const float rx = dxa + t * ux;
+    const float ry = dya + t * uy;
+    return rx * rx + ry * ry;
 }
 
 // Candidate test of one (pixel, face) pair against the current last key,
@@ -440,177 +479,245 @@ __device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float 
     kk = ((uint64_t)__float_as_uint(z) << 32) | (uint32_t)r.face;
     if (!(kk < last)) return false;
     if (inside) return true;
-    float d0, d1, d2, t, rx, ry;
-    edge_distance(px, py, r.x0, r.y0, r.x1, r.y1, r.il0, d0, t, rx, ry);
-    edge_distance(px, py, r.x1, r.y1, r.x2, r.y2, r.il1, d1, t, rx, ry);
-    edge_distance(px, py, r.x2, r.y2, r.x0, r.y0, r.il2, d2, t, rx, ry);
+    const float d0 = edge_dist2(dx0, dy0, r.x1 - r.x0, r.y1 - r.y0, r.il0);
+    const float d1 = edge_dist2(dx1, dy1, r.x2 - r.x1, r.y2 - r.y1, r.il1);
+    const float d2 = edge_dist2(dx2, dy2, r.x0 - r.x2, r.y0 - r.y2, r.il2);
     float d = d0;
     d = d1 < d ? d1 : d;
     d = d2 < d ? d2 : d;
     return d < blur;
 }
 
-// One workgroup per bin (visited heaviest first), one thread per pixel.
+// Smallest of the keys held by the four lanes of an aligned lane quad.
+__device__ __forceinline__ uint64_t quad_min(uint64_t x) {
+    uint64_t y = __shfl_xor(x, 1);
+    x = y < x ? y : x;
+    y = __shfl_xor(x, 2);
+    return y < x ? y : x;
+}
+
+// Merge the sorted lists of the lane `mask` apart into this lane's: both
+// lanes end with the K smallest keys of the two (disjoint) lists.
+template <int KMAX>
+__device__ __forceinline__ void merge_with_lane(uint64_t (&key)[KMAX], int mask) {
+    uint64_t other[KMAX];
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q) other[q] = __shfl_xor(key[q], mask);
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q)
+        if (other[q] < key[KMAX - 1]) topk_insert<KMAX>(key, other[q]);
+}
+
+// Fine pass: one workgroup per work item, in the heaviest-first order of
+// bin_scan (the grid has room for four items per bin; the workgroups past
+// the item count return at once).
+//
+// A whole-bin item gives each thread one pixel of the 16x16 bin; each wave
+// owns an 8x8 quarter, whose pixels' face sets overlap more than those of
+// four full bin rows would. A quarter item gives each of its 64 pixels four
+// lanes (an aligned lane quad, the pixels of a wave forming a 4x4 block);
+// lane s of the quad takes the faces of list positions 64s..64s+63 of every
+// round and keeps its own top-K, the quad shares the smallest of the four
+// K-th keys as its pruning bound (the K-th of any lane bounds the K-th of
+// their union from above), and the four lists are merged at the end.
+//
 // Each round stages up to 256 of the bin's faces in LDS (one per thread).
 // Every wave then describes the pixel boxes of its 64 faces with ballots:
 // colmask[c] has bit u set when face slot u's box covers bin column c, and
 // rowmask[r] likewise for bin row r. A pixel's candidate faces in the round
-// are colmask[its column] & rowmask[its row], so each thread evaluates only
+// are colmask[its column] & rowmask[its row], so each lane evaluates only
 // the faces whose box contains its pixel. With a depth-sorted list a pixel
-// stops at the first face whose depth lower bound exceeds its last key, and
-// the workgroup stops when all its pixels have.
-// The K output slots of each bin row are then written slot-linearly (lane
-// q writes slot q of the row's contiguous 16*K-slot run) after the keys are
-// exchanged through LDS, so that stores are contiguous across lanes.
+// stops at the first round whose depth lower bound exceeds its last key, and
+// the workgroup stops the item when all its pixels have.
+// The K output slots of each row of the item's region are then written
+// slot-linearly (lane q writes slot q of the row's contiguous run) after the
+// keys are exchanged through LDS, so that stores are contiguous across lanes.
 template <int KMAX>
-__global__ __launch_bounds__(kFineThreads) void fine_raster(
+__global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 7 : 1, 8))) void fine_raster(
     const FaceRec* __restrict__ recs, int64_t F, const int64_t* __restrict__ off,
-    const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const int32_t* __restrict__ perm,
-    const int32_t* __restrict__ entries, const float* __restrict__ round_lb, int64_t capacity, int32_t H,
-    int32_t W, int32_t K, float blur, int32_t nbx, int32_t nby, int64_t* __restrict__ pix_to_face,
-    float* __restrict__ zbuf, float* __restrict__ bary, float* __restrict__ dists) {
+    const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
+    WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
+    int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, int32_t nbx, int32_t nby,
+    int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
+    float* __restrict__ dists) {
     __shared__ FaceRec srec[kFineThreads];
     __shared__ uint64_t colmask[kBin][kFineThreads / 64];
     __shared__ uint64_t rowmask[kBin][kFineThreads / 64];
-    const int64_t b = perm[blockIdx.x];
-    const int64_t per_img = (int64_t)nbx * nby;
-    const int64_t n = b / per_img;
-    const int rem = (int)(b - n * per_img);
-    const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+    __shared__ float szlo[kFineThreads];
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
-    const int il = t / kBin, jl = t % kBin;
-    const int i = by * kBin + il;
-    const int j = bx * kBin + jl;
-    const bool valid = (i < H) && (j < W);
-    const float px = pixel_centre(j, W);
-    const float py = pixel_centre(i, H);
+    const int32_t n_items = hdr->fine_items;
+    const int64_t per_img = (int64_t)nbx * nby;
 
-    uint64_t key[KMAX];
+    {
+        if ((int64_t)blockIdx.x >= (int64_t)n_items) return;
+        const uint32_t code = items[blockIdx.x];
+        const int64_t b = (int64_t)(code >> 3);
+        const int part = (int)(code & 7u);
+        const bool quarter = part != kItemWhole;
+        const int64_t n = b / per_img;
+        const int rem = (int)(b - n * per_img);
+        const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+
+        // region of the item inside the bin, and this thread's pixel
+        const int reg_r = quarter ? (part >> 1) * (kBin / 2) : 0;
+        const int reg_c = quarter ? (part & 1) * (kBin / 2) : 0;
+        const int reg_w = quarter ? kBin / 2 : kBin;
+        const int sub = quarter ? (lane & 3) : 0;
+        int il, jl;
+        if (quarter) {
+            const int p = lane >> 2;   // 0..15: 4x4 block of the wave
+            il = reg_r + (wave >> 1) * 4 + (p >> 2);
+            jl = reg_c + (wave & 1) * 4 + (p & 3);
+        } else {
+            il = (wave >> 1) * (kBin / 2) + (lane >> 3);
+            jl = (wave & 1) * (kBin / 2) + (lane & 7);
+        }
+        const int i = by * kBin + il;
+        const int j = bx * kBin + jl;
+        const bool valid = (i < H) && (j < W);
+        const float px = pixel_centre(j, W);
+        const float py = pixel_centre(i, H);
+        const int w_lo = quarter ? sub : 0;
+        const int w_hi = quarter ? sub + 1 : kFineThreads / 64;
+
+        uint64_t key[KMAX];
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) key[q] = ~0ull;
+        for (int q = 0; q < KMAX; ++q) key[q] = ~0ull;
 
-    const int32_t cnt = count[b];
-    const int64_t o = offset[b];
-    const bool list_mode = (o + cnt <= capacity);
-    const bool sorted = list_mode && cnt <= kSortMax;
-    const float* lb = round_lb + b * kRoundsPerBin;
-    int64_t f0 = off[n], f1 = off[n + 1];
-    f0 = f0 < 0 ? 0 : f0;
-    f1 = f1 > F ? F : f1;
-    const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
-    bool done = !valid;
+        const int32_t cnt = count[b];
+        const int64_t o = offset[b];
+        const bool list_mode = (o + cnt <= capacity);
+        const bool sorted = list_mode && cnt <= kSortMax;
+        const float* lb = round_lb + b * kRoundsPerBin;
+        int64_t f0 = off[n], f1 = off[n + 1];
+        f0 = f0 < 0 ? 0 : f0;
+        f1 = f1 > F ? F : f1;
+        const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
+        bool done = !valid;
+        // pruning bound: this lane's last key, or the quad's smallest
+        uint64_t bound = ~0ull;
 
-    for (int64_t base = 0; base < total; base += kFineThreads) {
-        // Every face from this round on has zmin >= lb[round]; a pixel whose
-        // last key is below that bound (with the rounding margin of the
-        // depth interpolation) is finished.
-        if (sorted && !done) {
-            const float zl = lb[base / kFineThreads] * (1.0f - 0x1.0p-19f) - 1e-30f;
-            if (zl > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) done = true;
-        }
-        if (__syncthreads_count(!done) == 0) break;
-        int64_t q = base + t;
-        bool live = false;
-        int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
-        if (q < total) {
-            int64_t fid = list_mode ? (int64_t)entries[o + q] : f0 + q;
-            FaceRec r = recs[fid];
-            srec[t] = r;
-            if (r.face >= 0) {
-                c0 = max((r.box_lo & 0xffff) - bx * kBin, 0);
-                c1 = min((r.box_hi & 0xffff) - bx * kBin, kBin - 1);
-                r0 = max((r.box_lo >> 16) - by * kBin, 0);
-                r1 = min((r.box_hi >> 16) - by * kBin, kBin - 1);
-                live = (c0 <= c1) && (r0 <= r1);
+        for (int64_t base = 0; base < total; base += kFineThreads) {
+            if (quarter) bound = quad_min(key[KMAX - 1]);
+            else bound = key[KMAX - 1];
+            // Every face from this round on has zmin >= lb[round]; a pixel
+            // whose bound is below that (with the rounding margin of the
+            // depth interpolation) is finished.
+            if (sorted && !done) {
+                const float zl = lb[base / kFineThreads] * (1.0f - 0x1.0p-19f) - 1e-30f;
+                if (zl > __uint_as_float((uint32_t)(bound >> 32))) done = true;
             }
-        }
-#pragma unroll
-        for (int c = 0; c < kBin; ++c) {
-            uint64_t mc = __ballot(live && c0 <= c && c <= c1);
-            uint64_t mr = __ballot(live && r0 <= c && c <= r1);
-            if (lane == 0) {
-                colmask[c][wave] = mc;
-                rowmask[c][wave] = mr;
-            }
-        }
-        __syncthreads();
-        if (!done) {
-#pragma unroll 1
-            for (int w = 0; w < kFineThreads / 64; ++w) {
-                uint64_t m = colmask[jl][w] & rowmask[il][w];
-                while (m) {
-                    const int u = w * 64 + __builtin_ctzll(m);
-                    m &= m - 1;
-                    const FaceRec& r = srec[u];
-                    // Depth lower bound: z at any pixel is at least
-                    // min(z0, z1, z2) up to a few roundings, so a face whose
-                    // bound exceeds the last key cannot enter the list.
-                    const float zmin = fminf(r.z0, fminf(r.z1, r.z2));
-                    const float zlo = zmin * (1.0f - 0x1.0p-19f) - 1e-30f;
-                    if (zlo > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) continue;
-                    uint64_t kk;
-                    if (candidate_key(r, px, py, blur, key[KMAX - 1], kk)) topk_insert<KMAX>(key, kk);
+            if (__syncthreads_count(!done) == 0) break;
+            const int64_t q = base + t;
+            bool live = false;
+            int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
+            if (q < total) {
+                const int64_t fid = list_mode ? (int64_t)entries[o + q] : f0 + q;
+                const FaceRec r = recs[fid];
+                srec[t] = r;
+                // Depth lower bound: z at any pixel is at least
+                // min(z0, z1, z2) up to a few roundings, so a face whose
+                // bound exceeds a pixel's last key cannot enter its list.
+                szlo[t] = fminf(r.z0, fminf(r.z1, r.z2)) * (1.0f - 0x1.0p-19f) - 1e-30f;
+                if (r.face >= 0) {
+                    c0 = max((r.box_lo & 0xffff) - bx * kBin, 0);
+                    c1 = min((r.box_hi & 0xffff) - bx * kBin, kBin - 1);
+                    r0 = max((r.box_lo >> 16) - by * kBin, 0);
+                    r1 = min((r.box_hi >> 16) - by * kBin, kBin - 1);
+                    live = (c0 <= c1) && (r0 <= r1);
                 }
             }
-        }
-        __syncthreads();
-    }
-    __syncthreads();
-
-    // ---- output: exchange keys through LDS (reusing srec), then write each
-    // bin row's 16*K slots with consecutive lanes on consecutive slots
-    uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
-    constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
-    const int rows_per_pass = max(1, min(kBin, kBufKeys / (kBin * K)));
-    for (int r0 = 0; r0 < kBin; r0 += rows_per_pass) {
-        const int r1 = min(kBin, r0 + rows_per_pass);
-        if (il >= r0 && il < r1) {
-            uint64_t* dst = kbuf + ((il - r0) * kBin + jl) * K;
 #pragma unroll
-            for (int q = 0; q < KMAX; ++q)
-                if (q < K) dst[q] = key[q];
-        }
-        __syncthreads();
-        const int row_slots = kBin * K;
-        const int npass = (r1 - r0) * row_slots;
-        for (int e = t; e < npass; e += kFineThreads) {
-            const int rr = e / row_slots;
-            const int within = e - rr * row_slots;
-            const int jj = within / K;
-            const int gi = by * kBin + r0 + rr;
-            const int gj = bx * kBin + jj;
-            if (gi >= H || gj >= W) continue;
-            const int64_t so = (((int64_t)n * H + gi) * W + bx * kBin) * K + within;
-            const uint64_t kk = kbuf[e];
-            if (kk == ~0ull) {
-                pix_to_face[so] = -1;
-                zbuf[so] = -1.0f;
-                bary[3 * so + 0] = -1.0f;
-                bary[3 * so + 1] = -1.0f;
-                bary[3 * so + 2] = -1.0f;
-                dists[so] = -1.0f;
-            } else {
-                const int32_t face = (int32_t)(kk & 0xffffffffull);
-                PairState s;
-                eval_pair(recs[face], pixel_centre(gj, W), pixel_centre(gi, H), blur, true, s);
-                pix_to_face[so] = face;
-                zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
-                bary[3 * so + 0] = s.bh0;
-                bary[3 * so + 1] = s.bh1;
-                bary[3 * so + 2] = s.bh2;
-                dists[so] = s.inside ? -s.d2 : s.d2;
+            for (int c = 0; c < kBin; ++c) {
+                const uint64_t mc = __ballot(live && c0 <= c && c <= c1);
+                const uint64_t mr = __ballot(live && r0 <= c && c <= r1);
+                if (lane == 0) {
+                    colmask[c][wave] = mc;
+                    rowmask[c][wave] = mr;
+                }
             }
+            __syncthreads();
+            if (!done) {
+#pragma unroll 1
+                for (int w = w_lo; w < w_hi; ++w) {
+                    uint64_t m = colmask[jl][w] & rowmask[il][w];
+                    while (m) {
+                        const int u = w * 64 + __builtin_ctzll(m);
+                        m &= m - 1;
+                        const uint64_t last = key[KMAX - 1] < bound ? key[KMAX - 1] : bound;
+                        if (szlo[u] > __uint_as_float((uint32_t)(last >> 32))) continue;
+                        uint64_t kk;
+                        if (candidate_key(srec[u], px, py, blur, last, kk)) topk_insert<KMAX>(key, kk);
+                    }
+                }
+            }
+            __syncthreads();
         }
         __syncthreads();
+        if (quarter) {
+            merge_with_lane<KMAX>(key, 1);
+            merge_with_lane<KMAX>(key, 2);
+        }
+
+        // ---- output: exchange keys through LDS (reusing srec), then write
+        // each region row's reg_w*K slots with consecutive lanes on
+        // consecutive slots
+        uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
+        constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
+        const int row_slots = reg_w * K;
+        const int rows_per_pass = max(1, min(reg_w, kBufKeys / row_slots));
+        const bool writer = !quarter || sub == 0;
+        for (int ra = 0; ra < reg_w; ra += rows_per_pass) {
+            const int rb = min(reg_w, ra + rows_per_pass);
+            const int rr_me = il - reg_r;
+            if (writer && rr_me >= ra && rr_me < rb) {
+                uint64_t* dst = kbuf + ((rr_me - ra) * reg_w + (jl - reg_c)) * K;
+#pragma unroll
+                for (int q = 0; q < KMAX; ++q)
+                    if (q < K) dst[q] = key[q];
+            }
+            __syncthreads();
+            const int npass = (rb - ra) * row_slots;
+            for (int e = t; e < npass; e += kFineThreads) {
+                const int rr = e / row_slots;
+                const int within = e - rr * row_slots;
+                const int jj = within / K;
+                const int gi = by * kBin + reg_r + ra + rr;
+                const int gj = bx * kBin + reg_c + jj;
+                if (gi >= H || gj >= W) continue;
+                const int64_t so = (((int64_t)n * H + gi) * W + bx * kBin + reg_c) * K + within;
+                const uint64_t kk = kbuf[e];
+                if (kk == ~0ull) {
+                    pix_to_face[so] = -1;
+                    zbuf[so] = -1.0f;
+                    bary[3 * so + 0] = -1.0f;
+                    bary[3 * so + 1] = -1.0f;
+                    bary[3 * so + 2] = -1.0f;
+                    dists[so] = -1.0f;
+                } else {
+                    const int32_t face = (int32_t)(kk & 0xffffffffull);
+                    PairState st;
+                    eval_pair(recs[face], pixel_centre(gj, W), pixel_centre(gi, H), blur, true, st);
+                    pix_to_face[so] = face;
+                    zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
+                    bary[3 * so + 0] = st.bh0;
+                    bary[3 * so + 1] = st.bh1;
+                    bary[3 * so + 2] = st.bh2;
+                    dists[so] = st.inside ? -st.d2 : st.d2;
+                }
+            }
+            __syncthreads();
+        }
     }
 }
 
 template <int KMAX>
 static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const int32_t* count,
-                        const int64_t* offset, const int32_t* perm, const int32_t* entries, const float* round_lb) {
+                        const int64_t* offset, const uint32_t* items, WsHeader* hdr, const int32_t* entries,
+                        const float* round_lb) {
     fine_raster<KMAX><<<grid, kFineThreads, 0, a.stream>>>(
-        recs, a.F, a.off, count, offset, perm, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
+        recs, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
         (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
 }
 
@@ -641,7 +748,9 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
         timing_end(kKFaceSetup, a.stream);
     }
     timing_begin(kKBinScan, a.stream);
-    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, a.L.bins, block_live,
+    uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
+    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, items, a.L.bins,
+                                                 a.K <= kSplitMaxK ? 1 : 0, block_live,
                                                  a.F > 0 ? a.L.setup_blocks : 0, a.capacity, a.L.min_bytes, hdr);
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {
@@ -664,23 +773,27 @@ hipError_t launch_forward(const FwdArgs& a) {
     hipError_t err = launch_binning(a, true);
     if (err != hipSuccess) return err;
     char* ws = a.ws;
+    WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
     FaceRec* recs = reinterpret_cast<FaceRec*>(ws + a.L.off_records);
     int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
     int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
-    int32_t* perm = reinterpret_cast<int32_t*>(ws + a.L.off_perm);
+    uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
     float* round_lb = reinterpret_cast<float*>(ws + a.L.off_roundlb);
     int32_t* entries = reinterpret_cast<int32_t*>(ws + a.L.off_entries);
-    dim3 grid((unsigned)a.L.bins);
+    // room for every item: four per bin when bins may be split
+    dim3 grid((unsigned)(a.L.bins * (a.K <= kSplitMaxK ? 4 : 1)));
     timing_begin(kKFineRaster, a.stream);
-    if (a.K <= 1) launch_fine<1>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 2) launch_fine<2>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 4) launch_fine<4>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 8) launch_fine<8>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 10) launch_fine<10>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 16) launch_fine<16>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 32) launch_fine<32>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else if (a.K <= 50) launch_fine<50>(a, grid, recs, count, offset, perm, entries, round_lb);
-    else launch_fine<64>(a, grid, recs, count, offset, perm, entries, round_lb);
+#define DMR_FINE(KM) launch_fine<KM>(a, grid, recs, count, offset, items, hdr, entries, round_lb)
+    if (a.K <= 1) DMR_FINE(1);
+    else if (a.K <= 2) DMR_FINE(2);
+    else if (a.K <= 4) DMR_FINE(4);
+    else if (a.K <= 8) DMR_FINE(8);
+    else if (a.K <= 10) DMR_FINE(10);
+    else if (a.K <= 16) DMR_FINE(16);
+    else if (a.K <= 32) DMR_FINE(32);
+    else if (a.K <= 50) DMR_FINE(50);
+    else DMR_FINE(64);
+#undef DMR_FINE
     timing_end(kKFineRaster, a.stream);
     return hipGetLastError();
 }

@@ -2,7 +2,7 @@
 beyond the candidate count, culled and degenerate faces, exact depth ties,
 pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
-thousands of faces in one bin, faces using another mesh's vertices, invalid
+thousands of faces in one bin, heavy bins split into quarter items, faces using another mesh's vertices, invalid
 vertex indices, and the hand-worked cases."""
 
 import json
@@ -159,6 +159,21 @@ def one_face_over_all_bins():
 def thousands_in_one_bin():
     v, f = _soup(15, 5000, lo=-0.95, hi=-0.9, sigma=0.01)
     return v, f, [0, 5000], 64, 64, 8, 1e-4
+
+
+@case
+def dense_bins_split_into_quarters():
+    # about 3000 faces over one and a half bins: the heavy bins are worked
+    # as four 8x8 quarter items with four lanes per pixel
+    v, f = _soup(18, 3000, lo=-1.0, hi=-0.4, sigma=0.02)
+    return v, f, [0, 3000], 40, 56, 10, 1e-4
+
+
+@case
+def dense_split_bins_on_ragged_edge():
+    # split bins in the last bin row and column, partly outside the image
+    v, f = _soup(19, 2500, lo=0.75, hi=1.0, sigma=0.02)
+    return v, f, [0, 2500], 37, 45, 16, 5e-4
 
 
 @case
