@@ -185,7 +185,7 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
     if (slots > 0 && pix_to_face == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (V == 0) return DMR_SUCCESS;
     FwdLayout L = fwd_layout(N, F, H, W);
-    if (L.bins > (int64_t)UINT32_MAX) return DMR_ERROR_UNSUPPORTED;
+    if (L.bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;  // as in the forward pass
     const bool reuse = (flags & DMR_BWD_REUSE_FORWARD_WORKSPACE) != 0;
     if (reuse && slots > 0 && (workspace == nullptr || workspace_bytes < L.min_bytes))
         return DMR_ERROR_WORKSPACE_TOO_SMALL;

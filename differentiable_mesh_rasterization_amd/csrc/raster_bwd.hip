@@ -20,8 +20,10 @@
 
 namespace dmr {
 
-__global__ void zero_f32(float* p, int64_t n) {
+// Zero fill of grad_verts; also resets the tile queue counter when given.
+__global__ void zero_f32(float* p, int64_t n, int32_t* counter) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (counter && i == 0) *counter = 0;
     int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (; i < n; i += stride) p[i] = 0.0f;
 }
@@ -99,9 +101,10 @@ __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState&
 }
 
 constexpr int kBwdThreads = kBin * kBin;
-constexpr int kHashSize = 2048;
+constexpr int kHashBits = 10;
+constexpr int kHashSize = 1 << kHashBits;
 constexpr int kProbe = 32;
-constexpr int kListCap = 2048;   // compacted slots per chunk
+constexpr int kListCap = 1024;   // compacted slots per chunk
 
 // LDS sums are kept in 64-bit fixed point with kFixBits fractional bits: an
 // integer LDS atomic add is about 20x faster than a float one on gfx950 and
@@ -129,7 +132,7 @@ __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*h
     const float lim = kFixLimit;
     if (use_hash && fabsf(gx) < lim && fabsf(gy) < lim && fabsf(gz) < lim) {
         const int32_t vid = (int32_t)vi;
-        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - 11);
+        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - kHashBits);
         for (int p = 0; p < kProbe; ++p) {
             const int32_t cur = atomicCAS(&hkey[h], -1, vid);
             if (cur == -1 || cur == vid) {
@@ -168,19 +171,44 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
     return base + x - v;
 }
 
+// Tiles come from the grid (one workgroup per tile) or, with the forward's
+// workspace, from a queue in the forward's heaviest-first bin order: each
+// workgroup takes tiles until it meets a bin without faces (those come last
+// and have no filled slot) or the end of the order.
 __global__ __launch_bounds__(kBwdThreads) void backward_slots(
-    const FaceRec* __restrict__ recs, const float* __restrict__ verts, const int64_t* __restrict__ faces,
-    int64_t V, int64_t F, int32_t H, int32_t W, int32_t K, int32_t nbx, int32_t nby,
-    const int64_t* __restrict__ pix_to_face, const float* __restrict__ gzb, const float* __restrict__ gba,
-    const float* __restrict__ gds, float* __restrict__ grad_verts, int32_t use_hash_arg) {
+    const FaceRec* __restrict__ recs, const int32_t* __restrict__ bin_order, const int32_t* __restrict__ bin_count,
+    int32_t* __restrict__ queue, int64_t bins, const float* __restrict__ verts,
+    const int64_t* __restrict__ faces, int64_t V, int64_t F, int32_t H, int32_t W, int32_t K, int32_t nbx,
+    int32_t nby, const int64_t* __restrict__ pix_to_face, const float* __restrict__ gzb,
+    const float* __restrict__ gba, const float* __restrict__ gds, float* __restrict__ grad_verts,
+    int32_t use_hash_arg) {
     __shared__ int32_t hkey[kHashSize];
     __shared__ unsigned long long hval[kHashSize][3];
     __shared__ int32_t lface[kListCap];
     __shared__ uint16_t lslot[kListCap];   // tile pixel << 8 | slot
     __shared__ int wave_tot[kBwdThreads / 64];
+    __shared__ int64_t tile_s;
     const bool use_hash = use_hash_arg != 0;
-    const int64_t b = blockIdx.x;
     const int64_t per_img = (int64_t)nbx * nby;
+    for (int64_t next = blockIdx.x;; next += gridDim.x) {
+    if (queue) {
+        if (threadIdx.x == 0) {
+            const int32_t q = atomicAdd(queue, 1);
+            int64_t tb = -1;
+            if ((int64_t)q < bins) {
+                tb = bin_order[q];
+                if (bin_count[tb] == 0) tb = -1;
+            }
+            tile_s = tb;
+        }
+        __syncthreads();
+    } else if (threadIdx.x == 0) {
+        tile_s = next < bins ? next : -1;
+    }
+    __syncthreads();
+    const int64_t b = __builtin_amdgcn_readfirstlane((int32_t)tile_s);
+    __syncthreads();   // tile_s is rewritten by the next iteration
+    if (b < 0) break;
     const int64_t n = b / per_img;
     const int rem = (int)(b - n * per_img);
     const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
@@ -253,24 +281,48 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
             atomicAdd(&grad_verts[3 * (int64_t)vid + 2], from_fixed(hval[e][2]));
         }
     }
+    __syncthreads();   // the table is cleared for the next tile
+    }
 }
 
 hipError_t launch_backward(const BwdArgs& a) {
     const int64_t n3 = 3 * a.V;
+    const int64_t npix = a.N * (int64_t)a.H * a.W;
+    const bool work = npix > 0 && a.F > 0;
+    // With the forward's workspace, its per-face records (vertex positions,
+    // 1/A, inverse edge lengths) replace the per-slot gathers and divisions,
+    // and its bin order and counts drive a tile queue that skips empty bins.
+    const bool reuse = a.reuse_forward && work;
+    WsHeader* hdr = reuse ? reinterpret_cast<WsHeader*>(a.ws) : nullptr;
+    int32_t* queue = reuse ? &hdr->bwd_next : nullptr;
     if (n3 > 0) {
         timing_begin(kKZeroGrad, a.stream);
-        zero_f32<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_verts, n3);
+        zero_f32<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_verts, n3, queue);
         timing_end(kKZeroGrad, a.stream);
     }
-    const int64_t npix = a.N * (int64_t)a.H * a.W;
-    if (npix == 0 || a.F == 0) return hipGetLastError();
-    // With the forward's workspace, its per-face records (vertex positions,
-    // 1/A, inverse edge lengths) replace the per-slot gathers and divisions.
-    const FaceRec* recs = a.reuse_forward ? reinterpret_cast<const FaceRec*>(a.ws + a.L.off_records) : nullptr;
+    if (!work) return hipGetLastError();
+    const FaceRec* recs = reuse ? reinterpret_cast<const FaceRec*>(a.ws + a.L.off_records) : nullptr;
+    const int32_t* order = reuse ? reinterpret_cast<const int32_t*>(a.ws + a.L.off_perm) : nullptr;
+    const int32_t* count = reuse ? reinterpret_cast<const int32_t*>(a.ws + a.L.off_count) : nullptr;
+    int64_t grid = a.L.bins;
+    if (reuse) {
+        // as many workgroups as stay resident; each takes tiles from the queue
+        static int resident_per_cu = 0;
+        int dev = 0, cus = 0;
+        if (resident_per_cu == 0 &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident_per_cu, backward_slots, kBwdThreads, 0) !=
+                hipSuccess)
+            resident_per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        const int64_t resident = (int64_t)std::max(1, cus) * std::max(1, resident_per_cu);
+        grid = std::min<int64_t>(grid, resident);
+    }
     timing_begin(kKBackward, a.stream);
-    backward_slots<<<(unsigned)a.L.bins, kBwdThreads, 0, a.stream>>>(
-        recs, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.gz,
-        a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
+    backward_slots<<<(unsigned)grid, kBwdThreads, 0, a.stream>>>(
+        recs, order, count, queue, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
+        (int32_t)a.L.nby, a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
     timing_end(kKBackward, a.stream);
     return hipGetLastError();
 }
