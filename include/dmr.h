@@ -112,9 +112,13 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
  *              forward pass's workspace for these same inputs, unmodified
  *              since that call (workspace_bytes as given to it); its per-face
  *              records replace recomputing each face's data from verts and
- *              faces. The caller guarantees this; it is not checked, and any
- *              other content gives wrong gradients. With flags = 0 the
- *              workspace is not used and may be NULL.
+ *              faces, and its bin order and counts schedule the tiles (bins
+ *              without faces are skipped). The caller guarantees this; it is
+ *              not checked, and any other content gives wrong gradients. The
+ *              call writes one counter word of the workspace header (its tile
+ *              queue), so backward calls sharing a workspace must not overlap
+ *              in time. With flags = 0 the workspace is not used and may be
+ *              NULL.
  * Contributions are summed per 16x16 tile and vertex in LDS, then added to
  * grad_verts with float32 atomics, so the rounding of grad_verts may differ
  * between runs.
