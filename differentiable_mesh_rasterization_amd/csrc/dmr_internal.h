@@ -50,6 +50,16 @@ struct alignas(16) FaceRec {
 };
 static_assert(sizeof(FaceRec) == 80, "FaceRec layout");
 
+// What the binning passes need of a face (16 bytes): its pixel box (as in
+// FaceRec; empty for a face that is never a candidate), its mesh, and the
+// bits of its smallest vertex depth.
+struct alignas(16) FaceBin {
+    int32_t box_lo, box_hi;
+    int32_t mesh;
+    uint32_t zmin_bits;
+};
+static_assert(sizeof(FaceBin) == 16, "FaceBin layout");
+
 // Workspace header (first 256 bytes of the forward workspace).
 struct WsHeader {
     int64_t required_bytes;
@@ -70,7 +80,8 @@ static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 struct FwdLayout {
     int64_t bins, nbx, nby;
     int64_t setup_blocks;
-    size_t off_records, off_count, off_offset, off_cursor, off_perm, off_items, off_live, off_roundlb, off_entries;
+    size_t off_records, off_fbin, off_count, off_offset, off_cursor, off_perm, off_items, off_live, off_roundlb,
+        off_entries;
     size_t min_bytes;
 };
 
@@ -84,6 +95,8 @@ inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W) {
     size_t o = sizeof(WsHeader);
     L.off_records = o;
     o = align_up(o + (size_t)F * sizeof(FaceRec), 256);
+    L.off_fbin = o;
+    o = align_up(o + (size_t)F * sizeof(FaceBin), 256);
     L.off_count = o;
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
     L.off_offset = o;

@@ -19,10 +19,11 @@ namespace dmr {
 // zero fill (used instead of a memset so that the launch sequence holds
 // kernels only)
 // ---------------------------------------------------------------------------
-__global__ void zero_i32(int32_t* p, int64_t n) {
+__global__ void zero_i32x2(int32_t* p, int64_t n, int32_t* p2, int64_t n2) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    for (; i < n; i += stride) p[i] = 0;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = i; k < n; k += stride) p[k] = 0;
+    for (int64_t k = i; k < n2; k += stride) p2[k] = 0;
 }
 
 // ---------------------------------------------------------------------------
@@ -47,16 +48,19 @@ __device__ __forceinline__ int64_t mesh_of(const int64_t* __restrict__ off, int6
 __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     const float* __restrict__ verts, int64_t V, const int64_t* __restrict__ faces, int64_t F,
     const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W, float blur,
-    int32_t nbx, int32_t nby, FaceRec* __restrict__ recs, int32_t* __restrict__ bin_count,
-    int32_t* __restrict__ block_live, WsHeader* __restrict__ hdr) {
+    int32_t nbx, int32_t nby, FaceRec* __restrict__ recs, FaceBin* __restrict__ fbin,
+    int32_t* __restrict__ bin_count, int32_t* __restrict__ block_live, WsHeader* __restrict__ hdr) {
     __shared__ int32_t hist[kHistBins];
-    __shared__ int64_t home_s;
+    __shared__ int64_t home_s, home_lo, home_hi;
     __shared__ int32_t live_s;
     const int per_img = nbx * nby;
     const bool use_lds = per_img <= kHistBins;
     const int64_t f = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x;
     if (threadIdx.x == 0) {
-        home_s = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+        const int64_t h = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+        home_s = h;
+        home_lo = off[h];
+        home_hi = off[h + 1];
         live_s = 0;
     }
     if (use_lds)
@@ -69,8 +73,10 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         r.face = -1;
         r.box_lo = 0x7fff7fff;  // empty box: lo > hi
         r.box_hi = 0;
-        const int64_t n = mesh_of(off, N, f);
-        bool ok = (off[n] <= f) && (f < off[n + 1]);
+        // the faces of a block nearly always belong to the mesh of its first
+        const bool in_home = home_lo <= f && f < home_hi;
+        const int64_t n = in_home ? home : mesh_of(off, N, f);
+        bool ok = in_home || ((off[n] <= f) && (f < off[n + 1]));
         int64_t vi0 = faces[3 * f + 0], vi1 = faces[3 * f + 1], vi2 = faces[3 * f + 2];
         bool idx_ok = vi0 >= 0 && vi0 < V && vi1 >= 0 && vi1 < V && vi2 >= 0 && vi2 < V;
         if (!idx_ok) atomicOr(&hdr->flags, DMR_FLAG_BAD_VERTEX_INDEX);
@@ -130,6 +136,12 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
             }
         }
         recs[f] = r;
+        FaceBin fb;
+        fb.box_lo = r.box_lo;
+        fb.box_hi = r.box_hi;
+        fb.mesh = (int32_t)n;
+        fb.zmin_bits = __float_as_uint(fminf(z0, fminf(z1, z2)));
+        fbin[f] = fb;
     }
     // live-face count: one LDS atomic per wave, one plain store per block
     // (the scan kernel adds the per-block counts)
@@ -162,6 +174,46 @@ __device__ __forceinline__ int order_bucket(int32_t c) {
     return c <= 0 ? 32 : __clz(c);
 }
 
+// Exclusive prefix sum over a kScanThreads workgroup (wave scans, then the
+// wave totals scanned by the first wave).
+__device__ __forceinline__ int64_t block_exclusive_sum64(int64_t v, int64_t* wsum, int64_t& total) {
+    constexpr int kWaves = kScanThreads / 64;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int64_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int64_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int64_t y = lane < kWaves ? wsum[lane] : 0;
+        const int64_t y0 = y;
+#pragma unroll
+        for (int d = 1; d < kWaves; d <<= 1) {
+            const int64_t z = __shfl_up(y, d, 64);
+            if (lane >= d) y += z;
+        }
+        if (lane < kWaves) wsum[lane] = y - y0;
+        if (lane == kWaves - 1) wsum[kWaves] = y;
+    }
+    __syncthreads();
+    const int64_t r = wsum[wave] + x - v;
+    total = wsum[kWaves];
+    __syncthreads();
+    return r;
+}
+
+// Sum over a kScanThreads workgroup (wave sums, one LDS atomic per wave).
+__device__ __forceinline__ int64_t block_sum64(int64_t v, unsigned long long* acc) {
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    if ((threadIdx.x & 63) == 0) atomicAdd(acc, (unsigned long long)v);
+    __syncthreads();
+    const int64_t r = (int64_t)*acc;
+    return r;
+}
+
 __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restrict__ count,
                                                          int64_t* __restrict__ offset,
                                                          int32_t* __restrict__ cursor,
@@ -170,9 +222,8 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
                                                          const int32_t* __restrict__ block_live,
                                                          int64_t nblocks, int64_t capacity, size_t base_bytes,
                                                          WsHeader* __restrict__ hdr) {
-    __shared__ int64_t part[kScanThreads];
-    __shared__ int64_t ovf[kScanThreads];
-    __shared__ int64_t live_sum;
+    __shared__ int64_t wsum[kScanThreads / 64 + 1];
+    __shared__ unsigned long long acc_ovf, acc_live;
     __shared__ int32_t bucket_n[kOrderBuckets];
     __shared__ int32_t bucket_at[kOrderBuckets];
     __shared__ int32_t item_n[kOrderBuckets];
@@ -182,7 +233,10 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         bucket_n[t] = 0;
         item_n[t] = 0;
     }
-    if (t == 0) live_sum = 0;
+    if (t == 0) {
+        acc_ovf = 0;
+        acc_live = 0;
+    }
     const int64_t per = (bins + kScanThreads - 1) / kScanThreads;
     const int64_t b0 = t * per;
     const int64_t b1 = min(bins, b0 + per);
@@ -195,30 +249,33 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         const bool split = allow_split && c >= kSplitMin;
         atomicAdd(&item_n[order_bucket(split ? c / 4 : c)], split ? 4 : 1);
     }
-    part[t] = s;
-    __syncthreads();
-    if (t == 0) {
-        int32_t run = 0, irun = 0;
-        for (int q = 0; q < kOrderBuckets; ++q) {
-            bucket_at[q] = run;
-            run += bucket_n[q];
-            item_at[q] = irun;
-            irun += item_n[q];
+    int64_t total = 0;
+    int64_t run = block_exclusive_sum64(s, wsum, total);   // synchronises: the bucket counts are complete
+    if (t < 64) {
+        // bucket starts: exclusive sums over the kOrderBuckets buckets (first wave)
+        int x = t < kOrderBuckets ? bucket_n[t] : 0;
+        int y = t < kOrderBuckets ? item_n[t] : 0;
+        const int x0 = x, y0 = y;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int xs = __shfl_up(x, d, 64);
+            const int ys = __shfl_up(y, d, 64);
+            if (t >= d) {
+                x += xs;
+                y += ys;
+            }
         }
-        hdr->fine_items = irun;
+        if (t < kOrderBuckets) {
+            bucket_at[t] = x - x0;
+            item_at[t] = y - y0;
+        }
+        if (t == kOrderBuckets - 1) hdr->fine_items = y;
     }
-    // Hillis-Steele inclusive scan over the per-thread sums
-    for (int d = 1; d < kScanThreads; d <<= 1) {
-        int64_t v = (t >= d) ? part[t - d] : 0;
-        __syncthreads();
-        part[t] += v;
-        __syncthreads();
-    }
-    int64_t run = part[t] - s;  // exclusive prefix of this thread's chunk
+    __syncthreads();
     int64_t over = 0;
     for (int64_t b = b0; b < b1; ++b) {
         offset[b] = run;
-        int32_t c = count[b];
+        const int32_t c = count[b];
         if (run + c > capacity) ++over;
         run += c;
         cursor[b] = 0;
@@ -231,16 +288,12 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
             items[atomicAdd(&item_at[order_bucket(c)], 1)] = code | (uint32_t)kItemWhole;
         }
     }
-    ovf[t] = over;
     int64_t lv = 0;
     for (int64_t q = t; q < nblocks; q += kScanThreads) lv += block_live[q];
-    atomicAdd((unsigned long long*)&live_sum, (unsigned long long)lv);
-    __syncthreads();
+    const int64_t o = block_sum64(over, &acc_ovf);
+    const int64_t live = block_sum64(lv, &acc_live);
     if (t == 0) {
-        int64_t total = part[kScanThreads - 1];
-        hdr->live_faces = live_sum;
-        int64_t o = 0;
-        for (int q = 0; q < kScanThreads; ++q) o += ovf[q];
+        hdr->live_faces = live;
         offset[bins] = total;
         hdr->bin_entries = total;
         hdr->bin_capacity = capacity;
@@ -257,8 +310,7 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
 // in LDS, reserves each bin's range with one global atomic, then places its
 // faces at LDS-assigned positions inside the reserved ranges. The order of
 // faces inside a bin list does not affect any result.
-__global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceRec* __restrict__ recs, int64_t F,
-                                                          const int64_t* __restrict__ off, int64_t N,
+__global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restrict__ fbin, int64_t F,
                                                           const int32_t* __restrict__ count,
                                                           const int64_t* __restrict__ offset,
                                                           int32_t* __restrict__ cursor,
@@ -270,7 +322,7 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceRec* __restr
     const int per_img = nbx * nby;
     const bool use_lds = per_img <= kHistBins;
     const int64_t f = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x;
-    if (threadIdx.x == 0) home_s = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+    if (threadIdx.x == 0) home_s = fbin[(int64_t)blockIdx.x * kSetupThreads].mesh;
     if (use_lds)
         for (int q = threadIdx.x; q < per_img; q += kSetupThreads) hist[q] = 0;
     __syncthreads();
@@ -279,13 +331,10 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceRec* __restr
     int j0 = 0, i0 = 0, j1 = -1, i1 = -1;
     int64_t n = 0;
     if (f < F) {
-        const int32_t box_lo = recs[f].box_lo;
-        const int32_t box_hi = recs[f].box_hi;
-        if (recs[f].face >= 0) {
-            live = true;
-            n = mesh_of(off, N, f);
-            j0 = box_lo & 0xffff; i0 = box_lo >> 16; j1 = box_hi & 0xffff; i1 = box_hi >> 16;
-        }
+        const FaceBin fb = fbin[f];
+        j0 = fb.box_lo & 0xffff; i0 = fb.box_lo >> 16; j1 = fb.box_hi & 0xffff; i1 = fb.box_hi >> 16;
+        live = j0 <= j1 && i0 <= i1;
+        n = fb.mesh;
     }
     const bool local = live && use_lds && n == home;
     if (local)
@@ -326,6 +375,7 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceRec* __restr
 // list. Lists longer than kSortMax are left as they are (their bound is -inf).
 constexpr int kSortThreads = 256;
 constexpr int kSortBuckets = 256;
+static_assert(kSortBuckets == kSortThreads, "one bucket per sort thread");
 
 __device__ __forceinline__ uint32_t float_order_bits(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -335,16 +385,35 @@ __device__ __forceinline__ float order_bits_float(uint32_t o) {
     return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
 }
 
-__global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceRec* __restrict__ recs,
+constexpr int kSortPer = kSortMax / kSortThreads;   // list entries per thread
+
+// Exclusive prefix sum over a 256-thread workgroup (wave scans, then the
+// four wave totals).
+__device__ __forceinline__ int block256_exclusive_sum(int v, int* wsum) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0;
+#pragma unroll
+    for (int w = 0; w < kSortThreads / 64; ++w) before += (w < wave) ? wsum[w] : 0;
+    __syncthreads();
+    return before + x - v;
+}
+
+__global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restrict__ fbin,
                                                          const int32_t* __restrict__ count,
                                                          const int64_t* __restrict__ offset,
                                                          const int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ entries, int64_t capacity,
                                                          float* __restrict__ round_lb) {
-    __shared__ int32_t ids[kSortMax];
-    __shared__ float zs[kSortMax];
-    __shared__ int32_t sorted_ids[kSortMax];
     __shared__ int32_t hist[kSortBuckets];
+    __shared__ int wsum[kSortThreads / 64];
     __shared__ uint32_t lo_s, hi_s;
     __shared__ uint32_t rmin[kRoundsPerBin];
     const int64_t b = perm[blockIdx.x];
@@ -360,51 +429,51 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceRec* __restri
         lo_s = 0xffffffffu;
         hi_s = 0u;
     }
-    if (t < kSortBuckets) hist[t] = 0;
+    hist[t] = 0;
     if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
-    __syncthreads();
+    // the list stays in registers: entry q = t + kSortThreads * i
+    int32_t id[kSortPer];
+    uint32_t zb[kSortPer];   // order bits of zmin
     uint32_t mylo = 0xffffffffu, myhi = 0u;
-    for (int q = t; q < cnt; q += kSortThreads) {
-        const int32_t f = entries[o + q];
-        const FaceRec& r = recs[f];
-        const float zmin = fminf(r.z0, fminf(r.z1, r.z2));
-        ids[q] = f;
-        zs[q] = zmin;
-        const uint32_t ob = float_order_bits(zmin);
-        mylo = min(mylo, ob);
-        myhi = max(myhi, ob);
+#pragma unroll
+    for (int i = 0; i < kSortPer; ++i) {
+        const int q = t + kSortThreads * i;
+        id[i] = 0;
+        zb[i] = 0;
+        if (q < cnt) {
+            id[i] = entries[o + q];
+            zb[i] = float_order_bits(__uint_as_float(fbin[id[i]].zmin_bits));
+            mylo = min(mylo, zb[i]);
+            myhi = max(myhi, zb[i]);
+        }
     }
+    __syncthreads();
     atomicMin(&lo_s, mylo);
     atomicMax(&hi_s, myhi);
     __syncthreads();
     const float lo = order_bits_float(lo_s), hi = order_bits_float(hi_s);
     const float scale = (hi > lo) ? (float)kSortBuckets / (hi - lo) : 0.0f;
-    for (int q = t; q < cnt; q += kSortThreads) {
-        int k = (int)((zs[q] - lo) * scale);
+    int bk[kSortPer];
+#pragma unroll
+    for (int i = 0; i < kSortPer; ++i) {
+        int k = (int)((order_bits_float(zb[i]) - lo) * scale);
         k = k < 0 ? 0 : (k >= kSortBuckets ? kSortBuckets - 1 : k);
-        atomicAdd(&hist[k], 1);
+        bk[i] = k;
+        if (t + kSortThreads * i < cnt) atomicAdd(&hist[k], 1);
     }
     __syncthreads();
-    if (t == 0) {
-        int32_t run = 0;
-        for (int k = 0; k < kSortBuckets; ++k) {
-            const int32_t c = hist[k];
-            hist[k] = run;
-            run += c;
+    // bucket starts (one bucket per thread)
+    hist[t] = block256_exclusive_sum(hist[t], wsum);
+    __syncthreads();
+    // Every entry has been read: scatter the ids to their sorted places in
+    // the list, and note each round's smallest depth bound.
+#pragma unroll
+    for (int i = 0; i < kSortPer; ++i) {
+        if (t + kSortThreads * i < cnt) {
+            const int pos = atomicAdd(&hist[bk[i]], 1);
+            entries[o + pos] = id[i];
+            atomicMin(&rmin[pos / kFineThreads], zb[i]);
         }
-    }
-    __syncthreads();
-    for (int q = t; q < cnt; q += kSortThreads) {
-        int k = (int)((zs[q] - lo) * scale);
-        k = k < 0 ? 0 : (k >= kSortBuckets ? kSortBuckets - 1 : k);
-        const int pos = atomicAdd(&hist[k], 1);
-        sorted_ids[pos] = q;
-    }
-    __syncthreads();
-    for (int q = t; q < cnt; q += kSortThreads) {
-        const int src = sorted_ids[q];
-        entries[o + q] = ids[src];
-        atomicMin(&rmin[q / kFineThreads], float_order_bits(zs[src]));
     }
     __syncthreads();
     if (t == 0) {
@@ -541,9 +610,16 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
     float* __restrict__ dists) {
     __shared__ FaceRec srec[kFineThreads];
-    __shared__ uint64_t colmask[kBin][kFineThreads / 64];
-    __shared__ uint64_t rowmask[kBin][kFineThreads / 64];
-    __shared__ float szlo[kFineThreads];
+    // the round's masks and depth bounds; the output phase reuses the same
+    // bytes for its list of filled slots
+    __shared__ __align__(16) unsigned char aux[2 * kBin * (kFineThreads / 64) * 8 + kFineThreads * 4];
+    __shared__ int32_t nfill;
+    uint64_t(*colmask)[kFineThreads / 64] = reinterpret_cast<uint64_t(*)[kFineThreads / 64]>(aux);
+    uint64_t(*rowmask)[kFineThreads / 64] =
+        reinterpret_cast<uint64_t(*)[kFineThreads / 64]>(aux + kBin * (kFineThreads / 64) * 8);
+    float* szlo = reinterpret_cast<float*>(aux + 2 * kBin * (kFineThreads / 64) * 8);
+    uint16_t* olist = reinterpret_cast<uint16_t*>(aux);
+    constexpr int kOutList = (int)(sizeof(aux) / sizeof(uint16_t));
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int32_t n_items = hdr->fine_items;
@@ -660,14 +736,17 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             merge_with_lane<KMAX>(key, 2);
         }
 
-        // ---- output: exchange keys through LDS (reusing srec), then write
-        // each region row's reg_w*K slots with consecutive lanes on
-        // consecutive slots
+        // ---- output: exchange keys through LDS (reusing srec); write each
+        // region row's reg_w*K slots with consecutive lanes on consecutive
+        // slots (indices, depths and the padding of empty slots), collecting
+        // the filled slots in a list; then evaluate the listed slots densely
+        // for their barycentrics and distances.
         uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
         constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
         const int row_slots = reg_w * K;
-        const int rows_per_pass = max(1, min(reg_w, kBufKeys / row_slots));
+        const int rows_per_pass = max(1, min(reg_w, min(kBufKeys, kOutList) / row_slots));
         const bool writer = !quarter || sub == 0;
+        const int64_t row0 = ((int64_t)n * H + by * kBin + reg_r) * W + bx * kBin + reg_c;
         for (int ra = 0; ra < reg_w; ra += rows_per_pass) {
             const int rb = min(reg_w, ra + rows_per_pass);
             const int rr_me = il - reg_r;
@@ -677,35 +756,58 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 for (int q = 0; q < KMAX; ++q)
                     if (q < K) dst[q] = key[q];
             }
+            if (t == 0) nfill = 0;
             __syncthreads();
             const int npass = (rb - ra) * row_slots;
-            for (int e = t; e < npass; e += kFineThreads) {
+            for (int e0 = 0; e0 < npass; e0 += kFineThreads) {
+                const int e = e0 + t;
+                bool filled = false;
+                if (e < npass) {
+                    const int rr = e / row_slots;
+                    const int within = e - rr * row_slots;
+                    const int jj = within / K;
+                    if (by * kBin + reg_r + ra + rr < H && bx * kBin + reg_c + jj < W) {
+                        const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
+                        const uint64_t kk = kbuf[e];
+                        if (kk == ~0ull) {
+                            pix_to_face[so] = -1;
+                            zbuf[so] = -1.0f;
+                            bary[3 * so + 0] = -1.0f;
+                            bary[3 * so + 1] = -1.0f;
+                            bary[3 * so + 2] = -1.0f;
+                            dists[so] = -1.0f;
+                        } else {
+                            pix_to_face[so] = (int32_t)(kk & 0xffffffffull);
+                            zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
+                            filled = true;
+                        }
+                    }
+                }
+                const uint64_t bal = __ballot(filled);
+                int at = 0;
+                if (lane == 0 && bal) at = atomicAdd(&nfill, (int)__popcll(bal));
+                at = __shfl(at, 0, 64);
+                if (filled)
+                    olist[at + __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                         __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u))] =
+                        (uint16_t)e;
+            }
+            __syncthreads();
+            const int nf = nfill;
+            for (int x = t; x < nf; x += kFineThreads) {
+                const int e = olist[x];
                 const int rr = e / row_slots;
                 const int within = e - rr * row_slots;
                 const int jj = within / K;
-                const int gi = by * kBin + reg_r + ra + rr;
-                const int gj = bx * kBin + reg_c + jj;
-                if (gi >= H || gj >= W) continue;
-                const int64_t so = (((int64_t)n * H + gi) * W + bx * kBin + reg_c) * K + within;
-                const uint64_t kk = kbuf[e];
-                if (kk == ~0ull) {
-                    pix_to_face[so] = -1;
-                    zbuf[so] = -1.0f;
-                    bary[3 * so + 0] = -1.0f;
-                    bary[3 * so + 1] = -1.0f;
-                    bary[3 * so + 2] = -1.0f;
-                    dists[so] = -1.0f;
-                } else {
-                    const int32_t face = (int32_t)(kk & 0xffffffffull);
-                    PairState st;
-                    eval_pair(recs[face], pixel_centre(gj, W), pixel_centre(gi, H), blur, true, st);
-                    pix_to_face[so] = face;
-                    zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
-                    bary[3 * so + 0] = st.bh0;
-                    bary[3 * so + 1] = st.bh1;
-                    bary[3 * so + 2] = st.bh2;
-                    dists[so] = st.inside ? -st.d2 : st.d2;
-                }
+                const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
+                const int32_t face = (int32_t)(kbuf[e] & 0xffffffffull);
+                PairState st;
+                eval_pair(recs[face], pixel_centre(bx * kBin + reg_c + jj, W),
+                          pixel_centre(by * kBin + reg_r + ra + rr, H), blur, true, st);
+                bary[3 * so + 0] = st.bh0;
+                bary[3 * so + 1] = st.bh1;
+                bary[3 * so + 2] = st.bh2;
+                dists[so] = st.inside ? -st.d2 : st.d2;
             }
             __syncthreads();
         }
@@ -725,6 +827,7 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     char* ws = a.ws;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
     FaceRec* recs = reinterpret_cast<FaceRec*>(ws + a.L.off_records);
+    FaceBin* fbin = reinterpret_cast<FaceBin*>(ws + a.L.off_fbin);
     int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
     int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
     int32_t* cursor = reinterpret_cast<int32_t*>(ws + a.L.off_cursor);
@@ -736,15 +839,15 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     // header + bin counts to zero (header words are int32-sized multiples)
     {
         timing_begin(kKZeroFwd, a.stream);
-        zero_i32<<<64, 256, 0, a.stream>>>(reinterpret_cast<int32_t*>(hdr), (int64_t)(sizeof(WsHeader) / 4));
-        zero_i32<<<(unsigned)std::min<int64_t>(1024, (a.L.bins + 255) / 256 + 1), 256, 0, a.stream>>>(count, a.L.bins);
+        zero_i32x2<<<(unsigned)std::min<int64_t>(1024, (a.L.bins + 255) / 256 + 1), 256, 0, a.stream>>>(
+            reinterpret_cast<int32_t*>(hdr), (int64_t)(sizeof(WsHeader) / 4), count, a.L.bins);
         timing_end(kKZeroFwd, a.stream);
     }
     if (a.F > 0) {
         timing_begin(kKFaceSetup, a.stream);
         face_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
             a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, (int32_t)a.L.nbx, (int32_t)a.L.nby, recs,
-            count, block_live, hdr);
+            fbin, count, block_live, hdr);
         timing_end(kKFaceSetup, a.stream);
     }
     timing_begin(kKBinScan, a.stream);
@@ -755,14 +858,13 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {
         timing_begin(kKBinFill, a.stream);
-        bin_fill<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(recs, a.F, a.off, a.N, count, offset, cursor,
-                                                                      entries, a.capacity, (int32_t)a.L.nbx,
-                                                                      (int32_t)a.L.nby);
+        bin_fill<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
+            fbin, a.F, count, offset, cursor, entries, a.capacity, (int32_t)a.L.nbx, (int32_t)a.L.nby);
         timing_end(kKBinFill, a.stream);
     }
     if (a.F > 0 && sort) {
         timing_begin(kKBinSort, a.stream);
-        bin_sort<<<(unsigned)a.L.bins, kSortThreads, 0, a.stream>>>(recs, count, offset, perm, entries, a.capacity,
+        bin_sort<<<(unsigned)a.L.bins, kSortThreads, 0, a.stream>>>(fbin, count, offset, perm, entries, a.capacity,
                                                                      round_lb);
         timing_end(kKBinSort, a.stream);
     }
