@@ -116,8 +116,14 @@ constexpr int kListCap = 1024;   // compacted slots per chunk
 constexpr int kFixBits = 28;
 constexpr float kFixLimit = 0x1.0p20f;
 
+// (double)v * 2^kFixBits is exact; adding 1.5 * 2^52 rounds it to the
+// nearest integer (ties to even), which then sits in the low mantissa bits
+// of the sum as a two's complement offset from those of 1.5 * 2^52 (valid
+// for magnitudes below 2^51, here below 2^48).
 __device__ __forceinline__ unsigned long long to_fixed(float v) {
-    return (unsigned long long)(long long)__builtin_rint((double)v * (double)(1ull << kFixBits));
+    const double kRound = 6755399441055744.0;   // 1.5 * 2^52
+    const double d = (double)v * (double)(1ull << kFixBits) + kRound;
+    return (unsigned long long)(__double_as_longlong(d) - __double_as_longlong(kRound));
 }
 __device__ __forceinline__ float from_fixed(unsigned long long x) {
     return (float)((double)(long long)x * (1.0 / (double)(1ull << kFixBits)));
