@@ -38,6 +38,58 @@ def algorithmic_bytes(w, filled_slots, live_faces, grads):
     return {"fine_raster": fine, "backward_slots": bwd, "fwd_total": fwd_total, "bwd_total": bwd}
 
 
+# Sources each timed kernel is built from: a traffic measurement is used only
+# while these files are unchanged since the counters were taken.
+KERNEL_SOURCES = {
+    "fine_raster": ("raster_fwd.hip", "dmr_internal.h"),
+    "backward_slots": ("raster_bwd.hip", "dmr_internal.h"),
+}
+
+
+def kernel_source_digest(kernel: str) -> str:
+    import hashlib
+
+    here = os.path.dirname(os.path.abspath(__file__))
+    csrc = os.path.join(here, "differentiable_mesh_rasterization_amd", "csrc")
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed counter summary of this
+    kernel and workload (FETCH_SIZE + WRITE_SIZE, calibrated against a plain
+    copy), or None when there is none or the kernel's sources changed since."""
+    here = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(here, "profiles", f"{kernel}_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("DATA "):
+                fields = dict(kv.split("=", 1) for kv in line.split()[1:])
+    if fields.get("source") != kernel_source_digest(kernel):
+        return None
+    return int(float(fields["fetch_bytes"]) + float(fields["write_bytes"]))
+
+
+def copy_calibration(nbytes: int, reps: int) -> None:
+    """A plain device copy of a known size, for calibrating the HBM byte
+    counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    import torch
+
+    dev = torch.device("cuda:0")
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": src.numel() * 4, "reps": reps}), flush=True)
+
+
 def cpu_baseline(w, grads_np, seconds: float):
     """The oracle, as it stands, on a bounded sample of the workload's pixels."""
     import numpy as np
@@ -83,7 +135,13 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
+
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration, 5)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this path has no multi-GPU mode "
@@ -160,7 +218,8 @@ def main():
         avg_s = ms / n * 1e-3
         achieved = alg[dominant] / avg_s / 1e9
         roofline = {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                    "traffic": measured_traffic(dominant, w.name),
                     "algorithmic_bytes_per_launch": alg[dominant], "avg_launch_us": round(avg_s * 1e6, 2)}
     line = {
         "metric": METRIC,

@@ -603,7 +603,7 @@ __device__ __forceinline__ void merge_with_lane(uint64_t (&key)[KMAX], int mask)
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
 template <int KMAX>
 __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 7 : 1, 8))) void fine_raster(
-    const FaceRec* __restrict__ recs, int64_t F, const int64_t* __restrict__ off,
+    const FaceRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t F, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
     int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, int32_t nbx, int32_t nby,
@@ -689,19 +689,23 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             bool live = false;
             int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
             if (q < total) {
+                // the face's pixel box, clipped to the item's region (empty
+                // for a face that is never a candidate); only faces that
+                // reach the region have their full record staged
                 const int64_t fid = list_mode ? (int64_t)entries[o + q] : f0 + q;
-                const FaceRec r = recs[fid];
-                srec[t] = r;
-                // Depth lower bound: z at any pixel is at least
-                // min(z0, z1, z2) up to a few roundings, so a face whose
-                // bound exceeds a pixel's last key cannot enter its list.
-                szlo[t] = fminf(r.z0, fminf(r.z1, r.z2)) * (1.0f - 0x1.0p-19f) - 1e-30f;
-                if (r.face >= 0) {
-                    c0 = max((r.box_lo & 0xffff) - bx * kBin, 0);
-                    c1 = min((r.box_hi & 0xffff) - bx * kBin, kBin - 1);
-                    r0 = max((r.box_lo >> 16) - by * kBin, 0);
-                    r1 = min((r.box_hi >> 16) - by * kBin, kBin - 1);
-                    live = (c0 <= c1) && (r0 <= r1);
+                const FaceBin fb = fbin[fid];
+                c0 = max((fb.box_lo & 0xffff) - bx * kBin, reg_c);
+                c1 = min((fb.box_hi & 0xffff) - bx * kBin, reg_c + reg_w - 1);
+                r0 = max((fb.box_lo >> 16) - by * kBin, reg_r);
+                r1 = min((fb.box_hi >> 16) - by * kBin, reg_r + reg_w - 1);
+                live = (c0 <= c1) && (r0 <= r1);
+                if (live) {
+                    const FaceRec r = recs[fid];
+                    srec[t] = r;
+                    // Depth lower bound: z at any pixel is at least
+                    // min(z0, z1, z2) up to a few roundings, so a face whose
+                    // bound exceeds a pixel's last key cannot enter its list.
+                    szlo[t] = fminf(r.z0, fminf(r.z1, r.z2)) * (1.0f - 0x1.0p-19f) - 1e-30f;
                 }
             }
 #pragma unroll
@@ -815,11 +819,11 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
 }
 
 template <int KMAX>
-static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const int32_t* count,
+static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const FaceBin* fbin, const int32_t* count,
                         const int64_t* offset, const uint32_t* items, WsHeader* hdr, const int32_t* entries,
                         const float* round_lb) {
     fine_raster<KMAX><<<grid, kFineThreads, 0, a.stream>>>(
-        recs, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
+        recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
         (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
 }
 
@@ -877,6 +881,7 @@ hipError_t launch_forward(const FwdArgs& a) {
     char* ws = a.ws;
     WsHeader* hdr = reinterpret_cast<WsHeader*>(ws);
     FaceRec* recs = reinterpret_cast<FaceRec*>(ws + a.L.off_records);
+    FaceBin* fbin = reinterpret_cast<FaceBin*>(ws + a.L.off_fbin);
     int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
     int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
     uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
@@ -885,7 +890,7 @@ hipError_t launch_forward(const FwdArgs& a) {
     // room for every item: four per bin when bins may be split
     dim3 grid((unsigned)(a.L.bins * (a.K <= kSplitMaxK ? 4 : 1)));
     timing_begin(kKFineRaster, a.stream);
-#define DMR_FINE(KM) launch_fine<KM>(a, grid, recs, count, offset, items, hdr, entries, round_lb)
+#define DMR_FINE(KM) launch_fine<KM>(a, grid, recs, fbin, count, offset, items, hdr, entries, round_lb)
     if (a.K <= 1) DMR_FINE(1);
     else if (a.K <= 2) DMR_FINE(2);
     else if (a.K <= 4) DMR_FINE(4);
