@@ -28,7 +28,8 @@ STATUS = {0: "DMR_SUCCESS", 1: "DMR_ERROR_INVALID_VALUE", 2: "DMR_ERROR_WORKSPAC
 EXPORTED = [
     "rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
     "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
-    "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_kernel_timing", "dmr_reset_kernel_timing",
+    "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
+    "dmr_reset_kernel_timing",
 ]
 
 
@@ -78,6 +79,8 @@ def lib(path: Optional[str] = None):
     L.dmr_kernel_name.argtypes = [I32]
     L.dmr_set_kernel_timing.restype = ctypes.c_int
     L.dmr_set_kernel_timing.argtypes = [I32]
+    L.dmr_set_kernel_timing_mask.restype = ctypes.c_int
+    L.dmr_set_kernel_timing_mask.argtypes = [ctypes.c_uint32]
     L.dmr_kernel_timing.restype = ctypes.c_int
     L.dmr_kernel_timing.argtypes = [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.dmr_reset_kernel_timing.restype = ctypes.c_int
@@ -292,6 +295,17 @@ def set_kernel_timing(enable: bool) -> None:
     rc = lib().dmr_set_kernel_timing(1 if enable else 0)
     if rc != 0:
         raise DmrError("dmr_set_kernel_timing", rc)
+
+
+def set_kernel_timing_only(names) -> None:
+    """Times only the named kernels (see kernel_names())."""
+    ids = kernel_names()
+    mask = 0
+    for n in names:
+        mask |= 1 << ids.index(n)
+    rc = lib().dmr_set_kernel_timing_mask(mask)
+    if rc != 0:
+        raise DmrError("dmr_set_kernel_timing_mask", rc)
 
 
 def reset_kernel_timing() -> None:

@@ -20,7 +20,7 @@ struct Pending {
 };
 
 struct Timing {
-    bool enabled = false;
+    uint32_t mask = 0;   // bit id set: kernel id is timed
     std::vector<Pending> pending[kKernelCount];
     std::vector<hipEvent_t> pool;
     double total_ms[kKernelCount] = {};
@@ -65,13 +65,13 @@ hipError_t drain(int id) {
 }  // namespace
 
 void timing_begin(KernelId id, hipStream_t s) {
-    if (!g_timing.enabled) return;
+    if (!(g_timing.mask >> id & 1u)) return;
     hipEvent_t e = take_event();
     if (e && hipEventRecord(e, s) == hipSuccess) g_timing.open_start[id] = e;
 }
 
 void timing_end(KernelId id, hipStream_t s) {
-    if (!g_timing.enabled || !g_timing.open_start[id]) return;
+    if (!(g_timing.mask >> id & 1u) || !g_timing.open_start[id]) return;
     hipEvent_t e = take_event();
     if (e && hipEventRecord(e, s) == hipSuccess) g_timing.pending[id].push_back({g_timing.open_start[id], e});
     g_timing.open_start[id] = nullptr;
@@ -227,7 +227,14 @@ const char* dmr_kernel_name(int32_t id) {
 
 dmr_status dmr_set_kernel_timing(int32_t enable) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_timing.enabled = enable != 0;
+    g_timing.mask = enable != 0 ? (1u << kKernelCount) - 1u : 0u;
+    return DMR_SUCCESS;
+}
+
+dmr_status dmr_set_kernel_timing_mask(uint32_t mask) {
+    if (mask >> kKernelCount) return DMR_ERROR_INVALID_VALUE;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    g_timing.mask = mask;
     return DMR_SUCCESS;
 }
 

@@ -169,6 +169,9 @@ const char* dmr_status_string(dmr_status s);
 int32_t dmr_kernel_count(void);
 const char* dmr_kernel_name(int32_t id);
 dmr_status dmr_set_kernel_timing(int32_t enable);
+/* Times only the kernels whose id bit is set in mask (bit i = kernel i);
+ * DMR_ERROR_INVALID_VALUE for bits at or above dmr_kernel_count(). */
+dmr_status dmr_set_kernel_timing_mask(uint32_t mask);
 dmr_status dmr_kernel_timing(int32_t id, double* total_ms, int64_t* launches);
 dmr_status dmr_reset_kernel_timing(void);
 

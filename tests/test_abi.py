@@ -125,3 +125,14 @@ def test_python_binding_fails_loudly_without_library(tmp_path):
 
     with pytest.raises(RuntimeError, match="not built"):
         pkg.lib(str(tmp_path / "missing.so"))
+
+
+def test_kernel_timing_mask(dmr):
+    lib = dmr.lib()
+    n = lib.dmr_kernel_count()
+    assert n >= 2 and "fine_raster" in dmr.kernel_names() and "backward_slots" in dmr.kernel_names()
+    assert lib.dmr_set_kernel_timing_mask(1 << n) == INVALID
+    assert lib.dmr_set_kernel_timing_mask((1 << n) - 1) == SUCCESS
+    assert lib.dmr_set_kernel_timing_mask(0) == SUCCESS
+    dmr.set_kernel_timing_only(["fine_raster"])
+    dmr.set_kernel_timing(False)
