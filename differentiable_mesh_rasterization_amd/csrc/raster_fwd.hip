@@ -56,12 +56,23 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     const int per_img = nbx * nby;
     const bool use_lds = per_img <= kHistBins;
     const int64_t f = (int64_t)blockIdx.x * kSetupThreads + threadIdx.x;
+    // home mesh: the one holding the block's first face, found by all
+    // threads at once (one round of loads instead of a binary search)
+    const int64_t first = (int64_t)blockIdx.x * kSetupThreads;
     if (threadIdx.x == 0) {
-        const int64_t h = mesh_of(off, N, (int64_t)blockIdx.x * kSetupThreads);
+        home_s = -1;
+        live_s = 0;
+    }
+    __syncthreads();
+    for (int64_t q = threadIdx.x; q < N; q += kSetupThreads)
+        if (off[q] <= first && first < off[q + 1]) home_s = q;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        int64_t h = home_s;
+        if (h < 0) h = mesh_of(off, N, first);   // offsets not covering the face
         home_s = h;
         home_lo = off[h];
         home_hi = off[h + 1];
-        live_s = 0;
     }
     if (use_lds)
         for (int q = threadIdx.x; q < per_img; q += kSetupThreads) hist[q] = 0;
@@ -374,8 +385,9 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restr
 // A pixel whose last key lies below a round's bound can skip the rest of the
 // list. Lists longer than kSortMax are left as they are (their bound is -inf).
 constexpr int kSortThreads = 256;
-constexpr int kSortBuckets = 256;
-static_assert(kSortBuckets == kSortThreads, "one bucket per sort thread");
+constexpr int kSortBuckets = 1024;
+constexpr int kBucketsPer = kSortBuckets / kSortThreads;   // buckets per sort thread
+static_assert(kSortBuckets % kSortThreads == 0, "whole buckets per sort thread");
 
 __device__ __forceinline__ uint32_t float_order_bits(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -429,7 +441,8 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
         lo_s = 0xffffffffu;
         hi_s = 0u;
     }
-    hist[t] = 0;
+#pragma unroll
+    for (int i = 0; i < kBucketsPer; ++i) hist[t * kBucketsPer + i] = 0;
     if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
     // the list stays in registers: entry q = t + kSortThreads * i
     int32_t id[kSortPer];
@@ -462,8 +475,22 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
         if (t + kSortThreads * i < cnt) atomicAdd(&hist[k], 1);
     }
     __syncthreads();
-    // bucket starts (one bucket per thread)
-    hist[t] = block256_exclusive_sum(hist[t], wsum);
+    // bucket starts: each thread owns kBucketsPer consecutive buckets
+    {
+        int c[kBucketsPer];
+        int local = 0;
+#pragma unroll
+        for (int i = 0; i < kBucketsPer; ++i) {
+            c[i] = hist[t * kBucketsPer + i];
+            local += c[i];
+        }
+        int run = block256_exclusive_sum(local, wsum);
+#pragma unroll
+        for (int i = 0; i < kBucketsPer; ++i) {
+            hist[t * kBucketsPer + i] = run;
+            run += c[i];
+        }
+    }
     __syncthreads();
     // Every entry has been read: scatter the ids to their sorted places in
     // the list, and note each round's smallest depth bound.
