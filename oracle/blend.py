@@ -1,0 +1,106 @@
+"""CPU oracle of the second stage: fusing each pixel's K kept faces into one
+RGBA value, and its backward pass (binary64 numpy).
+
+TEST INFRASTRUCTURE ONLY: the plain, slow definition the GPU blend is
+checked against. Only tests/, __graft_entry__.smoke() and the CPU-baseline
+leg of bench.py may import this module; it imports nothing from the GPU
+package.
+
+The pages say that the second stage of the rasterizer merges the influence
+of the several faces kept per pixel, which eases the discontinuity of hard
+rasterization (gptget.net summary, "Methodology" and "Technical
+Contribution"; nubint.ai review, "Proposed method"). They give no formula.
+The reading used here, written out per pixel over its filled slots k
+(pix_to_face >= 0; padded slots take no part):
+
+  coverage      p_k = 1 / (1 + exp(d_k / sigma)),   q_k = 1 - p_k = 1 / (1 + exp(-d_k / sigma))
+                (d_k = dists, the signed squared distance: < 0 inside)
+  silhouette    alpha = 1 - prod_k q_k                       (0 with no filled slot)
+  colour        zeta_k = (zfar - z_k) / (zfar - znear), zeta_max = max_k zeta_k
+                w_k = p_k exp((zeta_k - zeta_max) / gamma),  bg weight = exp((eps - zeta_max) / gamma)
+                rgb = (sum_k w_k c_k + bg weight * background) / (sum_k w_k + bg weight)
+                (rgb = background with no filled slot)
+
+c_k is the colour of face pix_to_face[k]. rgb does not depend on zeta_max
+(it scales every weight alike), so the backward pass holds it fixed.
+Gradients flow to zbuf and dists of filled slots (padded slots get 0).
+
+Parity unpinned: agreement with any existing library's blending numerics.
+"""
+
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+
+
+@dataclasses.dataclass
+class BlendParams:
+    sigma: float = 1e-4
+    gamma: float = 1e-4
+    znear: float = 1.0
+    zfar: float = 100.0
+    eps: float = 1e-10
+    background: tuple = (1.0, 1.0, 1.0)
+
+
+def _pixel_terms(p2f, zbuf, dists, colors, prm):
+    """Per-slot quantities of the definition above, for [P, K] inputs."""
+    filled = p2f >= 0
+    d = np.where(filled, dists.astype(np.float64), 0.0)
+    z = np.where(filled, zbuf.astype(np.float64), 0.0)
+    p = 1.0 / (1.0 + np.exp(d / prm.sigma))
+    q = 1.0 / (1.0 + np.exp(-d / prm.sigma))
+    p = np.where(filled, p, 0.0)
+    q = np.where(filled, q, 1.0)
+    zeta = (prm.zfar - z) / (prm.zfar - prm.znear)
+    any_filled = filled.any(axis=1)
+    zeta_max = np.where(any_filled, np.max(np.where(filled, zeta, -np.inf), axis=1), 0.0)
+    e = np.where(filled, np.exp(np.where(filled, (zeta - zeta_max[:, None]) / prm.gamma, 0.0)), 0.0)
+    w = p * e
+    bgw = np.exp((prm.eps - zeta_max) / prm.gamma)
+    c = colors.astype(np.float64)[np.where(filled, p2f, 0)]          # [P, K, 3]
+    c = np.where(filled[..., None], c, 0.0)
+    return filled, p, q, w, bgw, c, any_filled
+
+
+def blend_forward(p2f, zbuf, dists, colors, prm: BlendParams):
+    """rgba [..., 4] for outputs shaped [..., K] (pix_to_face, zbuf, dists)."""
+    shape = p2f.shape[:-1]
+    K = p2f.shape[-1]
+    P = int(np.prod(shape)) if shape else 1
+    p2f = p2f.reshape(P, K)
+    filled, p, q, w, bgw, c, any_filled = _pixel_terms(p2f, zbuf.reshape(P, K), dists.reshape(P, K), colors, prm)
+    alpha = 1.0 - np.prod(q, axis=1)
+    bg = np.asarray(prm.background, np.float64)
+    num = np.einsum("pk,pkc->pc", w, c) + bgw[:, None] * bg[None, :]
+    den = w.sum(axis=1) + bgw
+    rgb = num / den[:, None]
+    rgb = np.where(any_filled[:, None], rgb, bg[None, :])
+    alpha = np.where(any_filled, alpha, 0.0)
+    return np.concatenate([rgb, alpha[:, None]], axis=1).reshape(shape + (4,))
+
+
+def blend_backward(p2f, zbuf, dists, colors, prm: BlendParams, grad_rgba):
+    """(grad_zbuf, grad_dists), each shaped like zbuf, from grad_rgba [..., 4]."""
+    shape = p2f.shape
+    K = shape[-1]
+    P = p2f.size // K
+    p2f = p2f.reshape(P, K)
+    g = grad_rgba.reshape(P, 4).astype(np.float64)
+    filled, p, q, w, bgw, c, any_filled = _pixel_terms(p2f, zbuf.reshape(P, K), dists.reshape(P, K), colors, prm)
+    one_minus_alpha = np.prod(q, axis=1)
+    bg = np.asarray(prm.background, np.float64)
+    den = w.sum(axis=1) + bgw
+    rgb = (np.einsum("pk,pkc->pc", w, c) + bgw[:, None] * bg[None, :]) / den[:, None]
+    # d rgb / d w_k = (c_k - rgb) / den, contracted with the rgb gradient
+    gw = np.einsum("pc,pkc->pk", g[:, :3], c - rgb[:, None, :]) / den[:, None]
+    # w_k = p_k e_k: dw/dd = -w q / sigma, dw/dz = -w / ((zfar - znear) gamma)
+    gd = gw * (-w * q / prm.sigma)
+    gz = gw * (-w / ((prm.zfar - prm.znear) * prm.gamma))
+    # alpha = 1 - prod q: d alpha / d d_k = -(1 - alpha) p_k / sigma
+    gd = gd + g[:, 3:4] * (-one_minus_alpha[:, None] * p / prm.sigma)
+    gd = np.where(filled & any_filled[:, None], gd, 0.0)
+    gz = np.where(filled & any_filled[:, None], gz, 0.0)
+    return gz.reshape(shape), gd.reshape(shape)
