@@ -91,6 +91,47 @@ def copy_calibration(nbytes: int, reps: int) -> None:
     print(json.dumps({"copy_bytes": src.numel() * 4, "reps": reps}), flush=True)
 
 
+def blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, steps):
+    """The second stage (the K slots fused into RGBA) on the step's outputs,
+    forward and backward, timed with HIP events outside the timed step, with
+    its HBM roofline: 16 B per slot read (index, depth, distance), the face
+    colours once and 16 B per pixel written (forward); the backward also
+    reads 16 B and writes 8 B per slot."""
+    from workloads import blend_upstream_grads, face_colors
+
+    colors = torch.from_numpy(face_colors(w)).to(dev)
+    grad = torch.from_numpy(blend_upstream_grads(w)).to(dev)
+    prm = dmr.blend_params()
+    rgba = torch.empty(p2f.shape[:-1] + (4,), dtype=torch.float32, device=dev)
+    gz = torch.empty_like(zbuf)
+    gd = torch.empty_like(dists)
+    for _ in range(2):
+        dmr.dmr_blend_fwd(p2f, zbuf, dists, colors, prm, rgba)
+        dmr.dmr_blend_bwd(p2f, zbuf, dists, colors, prm, grad, gz, gd)
+    torch.cuda.synchronize()
+    dmr.set_kernel_timing_only(["blend_fwd", "blend_bwd"])
+    dmr.reset_kernel_timing()
+    for _ in range(steps):
+        dmr.dmr_blend_fwd(p2f, zbuf, dists, colors, prm, rgba)
+        dmr.dmr_blend_bwd(p2f, zbuf, dists, colors, prm, grad, gz, gd)
+    torch.cuda.synchronize()
+    kt = dmr.kernel_timing()
+    dmr.set_kernel_timing(False)
+    pixels = w.pixels
+    fwd_bytes = 16 * w.slots + 12 * w.F + 16 * pixels
+    bwd_bytes = 16 * w.slots + 12 * w.F + 16 * pixels + 8 * w.slots
+    out = {}
+    for name, nbytes in (("blend_fwd", fwd_bytes), ("blend_bwd", bwd_bytes)):
+        ms, n = kt[name]
+        us = ms / n * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        out[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    out["value"] = round(w.slots / ((out["blend_fwd"]["avg_us"] + out["blend_bwd"]["avg_us"]) * 1e-6) / 1e6, 1)
+    out["unit"] = "Mpix*K/s"
+    return out
+
+
 def cpu_baseline(w, grads_np, seconds: float):
     """The oracle, as it stands, on a bounded sample of the workload's pixels."""
     import numpy as np
@@ -258,6 +299,7 @@ def main():
         "fwd_bwd_hbm_frac": round((alg["fwd_total"] + alg["bwd_total"]) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "workspace": {k: stats[k] for k in ("required_bytes", "bin_entries", "overflow_bins", "live_faces")},
     }
+    line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gnp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

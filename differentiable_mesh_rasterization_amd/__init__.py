@@ -29,7 +29,7 @@ EXPORTED = [
     "rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
     "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
-    "dmr_reset_kernel_timing",
+    "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd",
 ]
 
 
@@ -37,6 +37,11 @@ class DmrError(RuntimeError):
     def __init__(self, fn: str, status: int):
         self.status = status
         super().__init__(f"{fn} failed: {STATUS.get(status, status)} ({status_string(status)})")
+
+
+class dmr_blend_params(ctypes.Structure):
+    _fields_ = [("sigma", ctypes.c_float), ("gamma", ctypes.c_float), ("znear", ctypes.c_float),
+                ("zfar", ctypes.c_float), ("eps", ctypes.c_float), ("background", ctypes.c_float * 3)]
 
 
 class dmr_stats(ctypes.Structure):
@@ -85,6 +90,11 @@ def lib(path: Optional[str] = None):
     L.dmr_kernel_timing.argtypes = [I32, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int64)]
     L.dmr_reset_kernel_timing.restype = ctypes.c_int
     L.dmr_reset_kernel_timing.argtypes = []
+    BP = ctypes.POINTER(dmr_blend_params)
+    L.dmr_blend_fwd.restype = ctypes.c_int
+    L.dmr_blend_fwd.argtypes = [P, P, P, I64, I32, P, I64, BP, P, P]
+    L.dmr_blend_bwd.restype = ctypes.c_int
+    L.dmr_blend_bwd.argtypes = [P, P, P, I64, I32, P, I64, BP, P, P, P, P]
     if path is None:
         _lib = L
     return L
@@ -197,6 +207,50 @@ def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
         _stream_handle(dev))
     if rc != 0:
         raise DmrError("rasterize_meshes_bwd", rc)
+
+
+def blend_params(sigma: float = 1e-4, gamma: float = 1e-4, znear: float = 1.0, zfar: float = 100.0,
+                 eps: float = 1e-10, background=(1.0, 1.0, 1.0)) -> dmr_blend_params:
+    return dmr_blend_params(sigma, gamma, znear, zfar, eps, (ctypes.c_float * 3)(*background))
+
+
+def _blend_inputs(pix_to_face, zbuf, dists, face_colors):
+    dev = pix_to_face.device
+    K = pix_to_face.shape[-1]
+    _check(pix_to_face, "pix_to_face", torch.int64, dev)
+    _check(zbuf, "zbuf", torch.float32, dev, tuple(pix_to_face.shape))
+    _check(dists, "dists", torch.float32, dev, tuple(pix_to_face.shape))
+    _check(face_colors, "face_colors", torch.float32, dev)
+    if face_colors.dim() != 2 or face_colors.shape[1] != 3:
+        raise ValueError("face_colors must be [F, 3]")
+    return dev, pix_to_face.numel() // K, K
+
+
+def dmr_blend_fwd(pix_to_face: torch.Tensor, zbuf: torch.Tensor, dists: torch.Tensor, face_colors: torch.Tensor,
+                  params: dmr_blend_params, rgba: torch.Tensor) -> None:
+    """C-ABI second-stage blend on preallocated device tensors (include/dmr.h):
+    rgba [..., 4] from the forward pass's [..., K] outputs."""
+    dev, P, K = _blend_inputs(pix_to_face, zbuf, dists, face_colors)
+    _check(rgba, "rgba", torch.float32, dev, tuple(pix_to_face.shape[:-1]) + (4,))
+    rc = lib().dmr_blend_fwd(_ptr(pix_to_face), _ptr(zbuf), _ptr(dists), P, K, _ptr(face_colors),
+                             face_colors.shape[0], ctypes.byref(params), _ptr(rgba), _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("dmr_blend_fwd", rc)
+
+
+def dmr_blend_bwd(pix_to_face: torch.Tensor, zbuf: torch.Tensor, dists: torch.Tensor, face_colors: torch.Tensor,
+                  params: dmr_blend_params, grad_rgba: torch.Tensor, grad_zbuf: torch.Tensor,
+                  grad_dists: torch.Tensor) -> None:
+    """C-ABI backward of the blend: grad_zbuf, grad_dists [..., K] from grad_rgba [..., 4]."""
+    dev, P, K = _blend_inputs(pix_to_face, zbuf, dists, face_colors)
+    _check(grad_rgba, "grad_rgba", torch.float32, dev, tuple(pix_to_face.shape[:-1]) + (4,))
+    _check(grad_zbuf, "grad_zbuf", torch.float32, dev, tuple(pix_to_face.shape))
+    _check(grad_dists, "grad_dists", torch.float32, dev, tuple(pix_to_face.shape))
+    rc = lib().dmr_blend_bwd(_ptr(pix_to_face), _ptr(zbuf), _ptr(dists), P, K, _ptr(face_colors),
+                             face_colors.shape[0], ctypes.byref(params), _ptr(grad_rgba), _ptr(grad_zbuf),
+                             _ptr(grad_dists), _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("dmr_blend_bwd", rc)
 
 
 # ----------------------------------------------------------------------------

@@ -33,6 +33,7 @@ std::mutex g_timing_mu;
 
 const char* const kKernelNames[kKernelCount] = {
     "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_slots",
+    "blend_fwd", "blend_bwd",
 };
 
 hipEvent_t take_event() {
@@ -199,6 +200,54 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
     a.reuse_forward = reuse;
     a.stream = stream;
     return launch_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+namespace {
+
+dmr_status check_blend(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
+                       const float* colors, int64_t F, const dmr_blend_params* params) {
+    if (P < 0 || F < 0 || K < 1 || params == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (K > DMR_MAX_K) return DMR_ERROR_UNSUPPORTED;
+    int64_t slots = 0;
+    if (mul_overflows(P, K, &slots) || slots > INT64_MAX / 3) return DMR_ERROR_UNSUPPORTED;
+    const dmr_blend_params& p = *params;
+    if (!(p.sigma > 0.0f) || !isfinite(p.sigma) || !(p.gamma > 0.0f) || !isfinite(p.gamma)) return DMR_ERROR_INVALID_VALUE;
+    if (!isfinite(p.znear) || !isfinite(p.zfar) || !(p.zfar > p.znear) || !isfinite(p.eps)) return DMR_ERROR_INVALID_VALUE;
+    for (int c = 0; c < 3; ++c)
+        if (!isfinite(p.background[c])) return DMR_ERROR_INVALID_VALUE;
+    if (P > 0 && (!pix_to_face || !zbuf || !dists)) return DMR_ERROR_INVALID_VALUE;
+    if (F > 0 && !colors) return DMR_ERROR_INVALID_VALUE;
+    return DMR_SUCCESS;
+}
+
+}  // namespace
+
+dmr_status dmr_blend_fwd(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
+                         const float* face_colors, int64_t F, const dmr_blend_params* params, float* rgba,
+                         hipStream_t stream) {
+    dmr_status st = check_blend(pix_to_face, zbuf, dists, P, K, face_colors, F, params);
+    if (st != DMR_SUCCESS) return st;
+    if (P == 0) return DMR_SUCCESS;
+    if (!rgba || reinterpret_cast<uintptr_t>(rgba) % 16 != 0) return DMR_ERROR_INVALID_VALUE;
+    BlendArgs a{};
+    a.pix_to_face = pix_to_face; a.zbuf = zbuf; a.dists = dists; a.P = P; a.K = K;
+    a.colors = face_colors; a.F = F; a.prm = *params; a.rgba = rgba; a.stream = stream;
+    return launch_blend_forward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+dmr_status dmr_blend_bwd(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
+                         const float* face_colors, int64_t F, const dmr_blend_params* params,
+                         const float* grad_rgba, float* grad_zbuf, float* grad_dists, hipStream_t stream) {
+    dmr_status st = check_blend(pix_to_face, zbuf, dists, P, K, face_colors, F, params);
+    if (st != DMR_SUCCESS) return st;
+    if (P == 0) return DMR_SUCCESS;
+    if (!grad_rgba || !grad_zbuf || !grad_dists || reinterpret_cast<uintptr_t>(grad_rgba) % 16 != 0)
+        return DMR_ERROR_INVALID_VALUE;
+    BlendArgs a{};
+    a.pix_to_face = pix_to_face; a.zbuf = zbuf; a.dists = dists; a.P = P; a.K = K;
+    a.colors = face_colors; a.F = F; a.prm = *params; a.grad_rgba = grad_rgba; a.grad_zbuf = grad_zbuf;
+    a.grad_dists = grad_dists; a.stream = stream;
+    return launch_blend_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
 }
 
 dmr_status dmr_workspace_stats(const void* workspace, dmr_stats* out, hipStream_t stream) {

@@ -210,6 +210,8 @@ enum KernelId : int32_t {
     kKFineRaster,
     kKZeroGrad,
     kKBackward,
+    kKBlendFwd,
+    kKBlendBwd,
     kKernelCount
 };
 
@@ -242,10 +244,22 @@ struct BwdArgs {
     hipStream_t stream;
 };
 
+struct BlendArgs {
+    const int64_t* pix_to_face; const float* zbuf; const float* dists;
+    int64_t P; int32_t K;
+    const float* colors; int64_t F;
+    dmr_blend_params prm;
+    float* rgba;
+    const float* grad_rgba; float* grad_zbuf; float* grad_dists;
+    hipStream_t stream;
+};
+
 // Launch wrappers with optional event timing; return hipSuccess or the error.
 hipError_t launch_binning(const FwdArgs& a, bool sort);
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a);
+hipError_t launch_blend_forward(const BlendArgs& a);
+hipError_t launch_blend_backward(const BlendArgs& a);
 
 // Timing hooks (api.hip).
 void timing_begin(KernelId id, hipStream_t s);

@@ -132,6 +132,48 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
                                 float* grad_verts,
                                 void* workspace, size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
+/*
+ * Second stage: fusing each pixel's kept faces (gptget.net summary,
+ * "Methodology": the second stage merges the influence of the several faces
+ * of a pixel, easing the discontinuity of rasterization; nubint.ai review,
+ * "Proposed method": per-pixel K-nearest-face influence). The pages give no
+ * formula; the library's reading, per pixel over its filled slots k
+ * (pix_to_face in [0, F)), is
+ *     p_k = 1 / (1 + exp(dists_k / sigma)),      alpha = 1 - prod_k (1 - p_k)
+ *     zeta_k = (zfar - zbuf_k) / (zfar - znear), zeta_max = max_k zeta_k
+ *     w_k = p_k exp((zeta_k - zeta_max) / gamma), w_bg = exp((eps - zeta_max) / gamma)
+ *     rgb = (sum_k w_k color[pix_to_face_k] + w_bg background) / (sum_k w_k + w_bg)
+ * and (background, 0) for a pixel without filled slots.
+ */
+typedef struct dmr_blend_params {
+    float sigma;          /* > 0, squared NDC units: sharpness of the coverage */
+    float gamma;          /* > 0: depth softness of the colour weights */
+    float znear, zfar;    /* zfar > znear: depth range of the normalised inverse depth */
+    float eps;            /* offset of the background weight */
+    float background[3];  /* RGB of uncovered pixels */
+} dmr_blend_params;
+
+/*   pix_to_face [P,K] int64, zbuf [P,K] float32, dists [P,K] float32: the
+ *              forward pass's outputs (P = N*H*W pixels, K slots each);
+ *              indices outside [0, F) count as empty slots.
+ *   face_colors [F,3] float32 RGB per face.
+ *   params     host pointer, read during the call; finite values, sigma > 0,
+ *              gamma > 0, zfar > znear (else DMR_ERROR_INVALID_VALUE).
+ *   rgba       [P,4] float32, 16-byte aligned, overwritten.
+ * Computed in binary32 with the device exp; P == 0 launches nothing. */
+dmr_status dmr_blend_fwd(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
+                         const float* face_colors, int64_t F, const dmr_blend_params* params, float* rgba,
+                         hipStream_t stream);
+
+/* Backward of dmr_blend_fwd for the same inputs: grad_rgba [P,4] float32
+ * (16-byte aligned) in,
+ * grad_zbuf [P,K] and grad_dists [P,K] float32 out (overwritten; 0 on empty
+ * slots). zeta_max is held fixed (rgb does not depend on it); no gradient
+ * flows to the colours or parameters. */
+dmr_status dmr_blend_bwd(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
+                         const float* face_colors, int64_t F, const dmr_blend_params* params,
+                         const float* grad_rgba, float* grad_zbuf, float* grad_dists, hipStream_t stream);
+
 /* Smallest forward workspace (bytes) for these sizes: face records and bin
  * tables, with room for no per-bin face list. 0 on invalid arguments. */
 size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W);

@@ -104,3 +104,26 @@ def blend_backward(p2f, zbuf, dists, colors, prm: BlendParams, grad_rgba):
     gd = np.where(filled & any_filled[:, None], gd, 0.0)
     gz = np.where(filled & any_filled[:, None], gz, 0.0)
     return gz.reshape(shape), gd.reshape(shape)
+
+
+def blend_backward_scale(p2f, zbuf, dists, colors, prm: BlendParams, grad_rgba):
+    """Per-slot sums of the absolute values of the terms blend_backward adds
+    up, shaped like zbuf: (scale of grad_zbuf, scale of grad_dists). A
+    binary32 evaluation of the same sums is off by a small multiple of the
+    unit roundoff times these, even where the terms cancel to zero."""
+    shape = p2f.shape
+    K = shape[-1]
+    P = p2f.size // K
+    p2f = p2f.reshape(P, K)
+    g = np.abs(grad_rgba.reshape(P, 4).astype(np.float64))
+    filled, p, q, w, bgw, c, any_filled = _pixel_terms(p2f, zbuf.reshape(P, K), dists.reshape(P, K), colors, prm)
+    one_minus_alpha = np.prod(q, axis=1)
+    bg = np.asarray(prm.background, np.float64)
+    den = w.sum(axis=1) + bgw
+    rgb = (np.einsum("pk,pkc->pc", w, c) + bgw[:, None] * bg[None, :]) / den[:, None]
+    gw = np.einsum("pc,pkc->pk", g[:, :3], np.abs(c) + np.abs(rgb)[:, None, :]) / den[:, None]
+    sd = gw * (w * q / prm.sigma) + g[:, 3:4] * (one_minus_alpha[:, None] * p / prm.sigma)
+    sz = gw * (w / ((prm.zfar - prm.znear) * prm.gamma))
+    sd = np.where(filled & any_filled[:, None], sd, 0.0)
+    sz = np.where(filled & any_filled[:, None], sz, 0.0)
+    return sz.reshape(shape), sd.reshape(shape)

@@ -136,3 +136,31 @@ def test_kernel_timing_mask(dmr):
     assert lib.dmr_set_kernel_timing_mask(0) == SUCCESS
     dmr.set_kernel_timing_only(["fine_raster"])
     dmr.set_kernel_timing(False)
+
+
+def _blend_call(dmr, fn="dmr_blend_fwd", P=10, K=4, F=3, rgba=0x1000, **prm):
+    base = dict(sigma=1e-4, gamma=1e-4, znear=1.0, zfar=100.0, eps=1e-10, background=(1.0, 1.0, 1.0))
+    base.update(prm)
+    p = dmr.blend_params(**base)
+    lib = dmr.lib()
+    fake = ctypes.c_void_p(0x1000)  # validation fails or succeeds before any device access
+    if fn == "dmr_blend_fwd":
+        return lib.dmr_blend_fwd(fake, fake, fake, P, K, fake, F, ctypes.byref(p), ctypes.c_void_p(rgba), None)
+    return lib.dmr_blend_bwd(fake, fake, fake, P, K, fake, F, ctypes.byref(p), ctypes.c_void_p(rgba), fake, fake,
+                             None)
+
+
+@pytest.mark.parametrize("fn", ["dmr_blend_fwd", "dmr_blend_bwd"])
+@pytest.mark.parametrize("kw, status", [
+    (dict(sigma=0.0), INVALID), (dict(sigma=-1.0), INVALID), (dict(gamma=0.0), INVALID),
+    (dict(zfar=1.0), INVALID), (dict(zfar=0.5), INVALID), (dict(eps=float("nan")), INVALID),
+    (dict(background=(0.0, float("inf"), 0.0)), INVALID), (dict(K=0), INVALID), (dict(K=65), UNSUPPORTED),
+    (dict(P=-1), INVALID), (dict(rgba=0x1004), INVALID), (dict(rgba=0), INVALID),
+])
+def test_blend_rejects_invalid_arguments(dmr, fn, kw, status):
+    assert _blend_call(dmr, fn, **kw) == status
+
+
+def test_blend_with_no_pixels_is_a_no_op(dmr):
+    assert _blend_call(dmr, "dmr_blend_fwd", P=0) == SUCCESS
+    assert _blend_call(dmr, "dmr_blend_bwd", P=0) == SUCCESS

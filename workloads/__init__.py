@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for the mesh rasterizer.
 
-This package only draws geometry and upstream gradients. It holds none of the
+This package only draws geometry, per-face colours and upstream gradients. It holds none of the
 rasterizer's arithmetic, so both the CPU oracle (through the tests) and the
 GPU path (through the tests and the benchmark) can consume the same arrays
 without sharing any code of the method itself.
@@ -14,4 +14,6 @@ from .meshes import (  # noqa: F401
     upstream_grads,
     sample_pixels,
     masked_upstream_grads,
+    face_colors,
+    blend_upstream_grads,
 )

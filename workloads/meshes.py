@@ -302,3 +302,15 @@ def masked_upstream_grads(w: Workload, pixel_ids: np.ndarray, seed: Optional[int
         else:
             out[g] = None
     return out
+
+
+def face_colors(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Seeded per-face RGB colours in [0, 1) for the second stage, [F, 3] float32."""
+    rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 104729))
+    return rng.random((w.F, 3), dtype=np.float32)
+
+
+def blend_upstream_grads(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Dense N(0,1) float32 gradients of the blended RGBA image, [N, H, W, 4]."""
+    rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 130363))
+    return rng.standard_normal((w.N, w.H, w.W, 4), dtype=np.float32)
