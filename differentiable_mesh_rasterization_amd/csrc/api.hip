@@ -208,6 +208,8 @@ dmr_status check_blend(const int64_t* pix_to_face, const float* zbuf, const floa
                        const float* colors, int64_t F, const dmr_blend_params* params) {
     if (P < 0 || F < 0 || K < 1 || params == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (K > DMR_MAX_K) return DMR_ERROR_UNSUPPORTED;
+    // face indices are staged as int32; one 64-pixel workgroup per grid entry
+    if (F > INT32_MAX || P > (int64_t)INT32_MAX * 64) return DMR_ERROR_UNSUPPORTED;
     int64_t slots = 0;
     if (mul_overflows(P, K, &slots) || slots > INT64_MAX / 3) return DMR_ERROR_UNSUPPORTED;
     const dmr_blend_params& p = *params;

@@ -160,7 +160,9 @@ typedef struct dmr_blend_params {
  *   params     host pointer, read during the call; finite values, sigma > 0,
  *              gamma > 0, zfar > znear (else DMR_ERROR_INVALID_VALUE).
  *   rgba       [P,4] float32, 16-byte aligned, overwritten.
- * Computed in binary32 with the device exp; P == 0 launches nothing. */
+ * K above DMR_MAX_K, F above INT32_MAX or P above 64 * INT32_MAX give
+ * DMR_ERROR_UNSUPPORTED. Computed in binary32 with the device exp; P == 0
+ * launches nothing. */
 dmr_status dmr_blend_fwd(const int64_t* pix_to_face, const float* zbuf, const float* dists, int64_t P, int32_t K,
                          const float* face_colors, int64_t F, const dmr_blend_params* params, float* rgba,
                          hipStream_t stream);
