@@ -38,6 +38,12 @@ def build(out_path: str = LIB_PATH, source_dir: str = _HERE, extra_flags=()) -> 
     return out_path
 
 
+# Settings bits of the oracle (raster_oracle_impl.h): perspective-correct
+# barycentrics, back-face culling, unclipped barycentrics returned.
+PERSPECTIVE = 0x2
+CULL_BACKFACES = 0x4
+UNCLIPPED_BARY = 0x8
+
 _lib = None
 
 
@@ -55,13 +61,14 @@ def _load(path: Optional[str] = None):
 def _bind(lib):
     P = ctypes.c_void_p
     I64 = ctypes.c_int64
+    U32 = ctypes.c_uint32
     for sfx, real in (("f32", ctypes.c_float), ("f64", ctypes.c_double)):
         fn = getattr(lib, f"oracle_raster_{sfx}")
         fn.restype = ctypes.c_int
-        fn.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, real, P, I64, P, P, P, P, P]
+        fn.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, real, U32, P, I64, P, P, P, P, P]
         fn = getattr(lib, f"oracle_backward_{sfx}")
         fn.restype = ctypes.c_int
-        fn.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, real, P, I64, P, P, P, P, P]
+        fn.argtypes = [P, I64, P, I64, P, I64, I64, I64, I64, real, U32, P, I64, P, P, P, P, P]
     lib.oracle_num_threads.restype = ctypes.c_int
     lib.oracle_num_threads.argtypes = []
     return lib
@@ -85,13 +92,14 @@ def num_threads(lib_path: Optional[str] = None) -> int:
 
 def rasterize(verts, faces, offsets, H: int, W: int, K: int, blur: float,
               pixels: Optional[np.ndarray] = None, precision: str = "f32",
-              with_state: bool = False, lib_path: Optional[str] = None):
+              with_state: bool = False, lib_path: Optional[str] = None, settings: int = 0):
     """Forward pass on all pixels (pixels=None, outputs [N,H,W,K...]) or on a
     list of flat pixel ids (outputs [len(pixels), K...]).
 
     Returns (pix_to_face int64, zbuf, bary, dists[, state int32]) as numpy
     arrays of float32 (precision 'f32') or float64 ('f64'). With 'f64' the
-    vertices are taken as float64 (float32 inputs widen exactly)."""
+    vertices are taken as float64 (float32 inputs widen exactly). `settings`
+    is a mask of PERSPECTIVE, CULL_BACKFACES and UNCLIPPED_BARY."""
     lib = _load(lib_path)
     verts, faces, offsets = _prep(verts, faces, offsets, precision)
     N = offsets.shape[0] - 1
@@ -111,7 +119,7 @@ def rasterize(verts, faces, offsets, H: int, W: int, K: int, blur: float,
     state = np.empty(shape, np.int32) if with_state else None
     fn = lib.oracle_raster_f32 if precision == "f32" else lib.oracle_raster_f64
     rc = fn(_ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(offsets), N,
-            H, W, K, float(blur), _ptr(pix), npix,
+            H, W, K, float(blur), int(settings), _ptr(pix), npix,
             _ptr(p2f), _ptr(zbuf), _ptr(bary), _ptr(dists), _ptr(state))
     if rc != 0:
         raise RuntimeError(f"oracle_raster_{precision} failed with code {rc}")
@@ -122,7 +130,7 @@ def rasterize(verts, faces, offsets, H: int, W: int, K: int, blur: float,
 def backward(verts, faces, offsets, H: int, W: int, K: int, blur: float, pix_to_face,
              grad_zbuf=None, grad_bary=None, grad_dists=None,
              pixels: Optional[np.ndarray] = None, precision: str = "f32",
-             lib_path: Optional[str] = None) -> np.ndarray:
+             lib_path: Optional[str] = None, settings: int = 0) -> np.ndarray:
     """Backward pass: returns grad_verts [V,3] as float64 (sum of the per-slot
     partials formed in `precision`). Gradient arrays match pix_to_face's
     layout ([N,H,W,K] for all pixels, [len(pixels), K] for a pixel list)."""
@@ -140,7 +148,7 @@ def backward(verts, faces, offsets, H: int, W: int, K: int, blur: float, pix_to_
     out = np.zeros((verts.shape[0], 3), np.float64)
     fn = lib.oracle_backward_f32 if precision == "f32" else lib.oracle_backward_f64
     rc = fn(_ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(offsets), N,
-            H, W, K, float(blur), _ptr(pix), npix, _ptr(p2f),
+            H, W, K, float(blur), int(settings), _ptr(pix), npix, _ptr(p2f),
             _ptr(gz), _ptr(gb), _ptr(gd), _ptr(out))
     if rc != 0:
         raise RuntimeError(f"oracle_backward_{precision} failed with code {rc}")

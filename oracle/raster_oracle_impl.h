@@ -34,7 +34,29 @@
  *   order            K smallest (z, global face index), ascending;
  *   padding          -1 in pix_to_face, zbuf, every bary component and dists;
  *   signed distance  dists = -d2 when inside, +d2 otherwise.
+ *
+ * Settings (bit mask `settings`; rocketrecap summary, "32:56 Technical Bug
+ * Fix", names a perspective_correct setting of the rasterizer, with no
+ * definition; the readings here are the library's):
+ *   0x2 perspective-correct: a face is a candidate only if all three vertex
+ *       depths are > 0; the clipped barycentrics c are weighted by the inverse
+ *       vertex depths, n_k = c_k z_{k+1} z_{k+2}, bh = n / (n0 + n1 + n2)
+ *       (this normalisation replaces the division by c0 + c1 + c2), and
+ *       z = sum bh_k z_k, i.e. 1 / z is interpolated linearly in screen space;
+ *   0x4 back-face culling: a face whose doubled area A is > 0 is skipped (A is
+ *       the z component of (v1 - v0) x (v2 - v0), so its normal points away
+ *       from the viewer, toward larger depth);
+ *   0x8 unclipped barycentrics: the returned bary are the barycentrics before
+ *       clipping (with 0x2, perspective-corrected the same way from the
+ *       unclipped values); depth, inclusion and order are unchanged.
+ * Settings 0 gives the conventions listed above.
  */
+#ifndef ORACLE_SETTINGS_DEFINED
+#define ORACLE_SETTINGS_DEFINED
+#define ORACLE_PERSPECTIVE 0x2u
+#define ORACLE_CULL_BACK 0x4u
+#define ORACLE_UNCLIPPED 0x8u
+#endif
 
 #ifndef R
 #error "define R (float or double) and SFX(name) before including"
@@ -52,6 +74,9 @@ typedef struct {
     int argmin;
     R d2;
     R c[3], S, invS, bh[3];
+    R n[3], D, invD;     /* perspective weights of c */
+    R out[3];            /* returned barycentrics */
+    R nr[3], Dr, invDr;  /* perspective weights of the unclipped b */
     R zp;   /* interpolated depth at the pixel */
     R dist; /* signed squared distance */
 } SFX(slot_t);
@@ -73,7 +98,7 @@ static R SFX(pixel_centre)(int64_t j, int64_t W) {
  * candidates.
  */
 static int SFX(eval_face)(const R* verts, int64_t V, const int64_t* faces, int64_t f,
-                          R px, R py, R blur, SFX(slot_t)* s) {
+                          R px, R py, R blur, uint32_t settings, SFX(slot_t)* s) {
     s->face = f;
     for (int k = 0; k < 3; ++k) {
         int64_t vi = faces[3 * f + k];
@@ -86,6 +111,8 @@ static int SFX(eval_face)(const R* verts, int64_t V, const int64_t* faces, int64
     /* Twice the signed area; zero means a degenerate face, which is skipped. */
     s->A = (s->x[1] - s->x[0]) * (s->y[2] - s->y[0]) - (s->y[1] - s->y[0]) * (s->x[2] - s->x[0]);
     if (s->A == (R)0) return 0;
+    if ((settings & ORACLE_CULL_BACK) && s->A > (R)0) return 0;
+    if ((settings & ORACLE_PERSPECTIVE) && !(s->z[0] > (R)0 && s->z[1] > (R)0 && s->z[2] > (R)0)) return 0;
     s->invA = (R)1 / s->A;
 
     for (int k = 0; k < 3; ++k) {
@@ -145,12 +172,29 @@ static int SFX(eval_face)(const R* verts, int64_t V, const int64_t* faces, int64
         if (c > (R)1) c = (R)1;
         s->c[k] = c;
     }
-    s->S = (s->c[0] + s->c[1]) + s->c[2];
-    s->invS = (R)1 / s->S;
-    for (int k = 0; k < 3; ++k) s->bh[k] = s->c[k] * s->invS;
+    if (settings & ORACLE_PERSPECTIVE) {
+        /* weight of vertex k: c_k / z_k, scaled by z0 z1 z2 */
+        for (int k = 0; k < 3; ++k) s->n[k] = (s->c[k] * s->z[(k + 1) % 3]) * s->z[(k + 2) % 3];
+        s->D = (s->n[0] + s->n[1]) + s->n[2];
+        s->invD = (R)1 / s->D;
+        for (int k = 0; k < 3; ++k) s->bh[k] = s->n[k] * s->invD;
+    } else {
+        s->S = (s->c[0] + s->c[1]) + s->c[2];
+        s->invS = (R)1 / s->S;
+        for (int k = 0; k < 3; ++k) s->bh[k] = s->c[k] * s->invS;
+    }
     s->zp = (s->bh[0] * s->z[0] + s->bh[1] * s->z[1]) + s->bh[2] * s->z[2];
     if (!(s->zp > (R)0)) return 0;
     s->dist = s->inside ? -s->d2 : s->d2;
+    for (int k = 0; k < 3; ++k) s->out[k] = s->bh[k];
+    if ((settings & ORACLE_UNCLIPPED) && (settings & ORACLE_PERSPECTIVE)) {
+        for (int k = 0; k < 3; ++k) s->nr[k] = (s->b[k] * s->z[(k + 1) % 3]) * s->z[(k + 2) % 3];
+        s->Dr = (s->nr[0] + s->nr[1]) + s->nr[2];
+        s->invDr = (R)1 / s->Dr;
+        for (int k = 0; k < 3; ++k) s->out[k] = s->nr[k] * s->invDr;
+    } else if (settings & ORACLE_UNCLIPPED) {
+        for (int k = 0; k < 3; ++k) s->out[k] = s->b[k];
+    }
     return 1;
 }
 
@@ -194,7 +238,7 @@ static int32_t SFX(slot_code)(const SFX(slot_t)* s) {
  */
 int SFX(oracle_raster)(const R* verts, int64_t V, const int64_t* faces, int64_t F,
                        const int64_t* offsets, int64_t N, int64_t H, int64_t W, int64_t K, R blur,
-                       const int64_t* pixels, int64_t npix,
+                       uint32_t settings, const int64_t* pixels, int64_t npix,
                        int64_t* pix_to_face, R* zbuf, R* bary, R* dists, int32_t* state) {
     if (V < 0 || F < 0 || N < 0 || H < 1 || W < 1 || K < 1) return 1;
     int64_t total = N * H * W;
@@ -224,7 +268,7 @@ int SFX(oracle_raster)(const R* verts, int64_t V, const int64_t* faces, int64_t 
             if (f1 > F) f1 = F;
             int64_t nc = 0;
             for (int64_t f = f0; f < f1; ++f) {
-                if (!SFX(eval_face)(verts, V, faces, f, px, py, blur, &s)) continue;
+                if (!SFX(eval_face)(verts, V, faces, f, px, py, blur, settings, &s)) continue;
                 if (nc == cap) {
                     cap *= 2;
                     cand = (SFX(cand_t)*)realloc(cand, sizeof(SFX(cand_t)) * (size_t)cap);
@@ -237,10 +281,10 @@ int SFX(oracle_raster)(const R* verts, int64_t V, const int64_t* faces, int64_t 
             for (int64_t k = 0; k < K; ++k) {
                 int64_t o = q * K + k;
                 if (k < nc) {
-                    SFX(eval_face)(verts, V, faces, cand[k].face, px, py, blur, &s);
+                    SFX(eval_face)(verts, V, faces, cand[k].face, px, py, blur, settings, &s);
                     pix_to_face[o] = cand[k].face;
                     zbuf[o] = s.zp;
-                    for (int c = 0; c < 3; ++c) bary[3 * o + c] = s.bh[c];
+                    for (int c = 0; c < 3; ++c) bary[3 * o + c] = s.out[c];
                     dists[o] = s.dist;
                     if (state) state[o] = SFX(slot_code)(&s);
                 } else {
@@ -267,7 +311,7 @@ int SFX(oracle_raster)(const R* verts, int64_t V, const int64_t* faces, int64_t 
  */
 int SFX(oracle_backward)(const R* verts, int64_t V, const int64_t* faces, int64_t F,
                          const int64_t* offsets, int64_t N, int64_t H, int64_t W, int64_t K, R blur,
-                         const int64_t* pixels, int64_t npix, const int64_t* pix_to_face,
+                         uint32_t settings, const int64_t* pixels, int64_t npix, const int64_t* pix_to_face,
                          const float* grad_zbuf, const float* grad_bary, const float* grad_dists,
                          double* grad_verts) {
     if (V < 0 || F < 0 || N < 0 || H < 1 || W < 1 || K < 1) return 1;
@@ -290,14 +334,16 @@ int SFX(oracle_backward)(const R* verts, int64_t V, const int64_t* faces, int64_
             int64_t o = q * K + k;
             int64_t f = pix_to_face[o];
             if (f < 0) continue;
-            if (f >= F || !SFX(eval_face)(verts, V, faces, f, px, py, blur, &s)) {
+            if (f >= F || !SFX(eval_face)(verts, V, faces, f, px, py, blur, settings, &s)) {
                 err = 3; /* pix_to_face does not come from a forward pass on these inputs */
                 continue;
             }
             R gz = grad_zbuf ? (R)grad_zbuf[o] : (R)0;
             R gd = grad_dists ? (R)grad_dists[o] : (R)0;
-            R gbh[3];
-            for (int c = 0; c < 3; ++c) gbh[c] = grad_bary ? (R)grad_bary[3 * o + c] : (R)0;
+            R gbh[3], gout[3];
+            for (int c = 0; c < 3; ++c) gout[c] = grad_bary ? (R)grad_bary[3 * o + c] : (R)0;
+            /* the returned barycentrics are bh unless they are the unclipped ones */
+            for (int c = 0; c < 3; ++c) gbh[c] = (settings & ORACLE_UNCLIPPED) ? (R)0 : gout[c];
 
             R gx[3] = {0, 0, 0}, gy[3] = {0, 0, 0}, gzv[3];
             /* depth: zp = sum bh[k] z[k] */
@@ -305,13 +351,36 @@ int SFX(oracle_backward)(const R* verts, int64_t V, const int64_t* faces, int64_
                 gzv[c] = gz * s.bh[c];
                 gbh[c] = gbh[c] + gz * s.z[c];
             }
-            /* renormalisation bh = c / S */
             R dot = (gbh[0] * s.bh[0] + gbh[1] * s.bh[1]) + gbh[2] * s.bh[2];
             R gb[3];
             for (int c = 0; c < 3; ++c) {
-                R gc = (gbh[c] - dot) * s.invS;
+                R gc;
+                if (settings & ORACLE_PERSPECTIVE) {
+                    /* bh = n / D, n_c = c_c z_{c+1} z_{c+2} */
+                    R gn = (gbh[c] - dot) * s.invD;
+                    int c1 = (c + 1) % 3, c2 = (c + 2) % 3;
+                    gc = gn * (s.z[c1] * s.z[c2]);
+                    gzv[c1] += gn * (s.c[c] * s.z[c2]);
+                    gzv[c2] += gn * (s.c[c] * s.z[c1]);
+                } else {
+                    /* renormalisation bh = c / S */
+                    gc = (gbh[c] - dot) * s.invS;
+                }
                 /* clip to [0,1]: passes the gradient only strictly inside the interval */
                 gb[c] = (s.b[c] > (R)0 && s.b[c] < (R)1) ? gc : (R)0;
+            }
+            if ((settings & ORACLE_UNCLIPPED) && (settings & ORACLE_PERSPECTIVE)) {
+                /* out = nr / Dr, nr_c = b_c z_{c+1} z_{c+2} */
+                R dotr = (gout[0] * s.out[0] + gout[1] * s.out[1]) + gout[2] * s.out[2];
+                for (int c = 0; c < 3; ++c) {
+                    R gn = (gout[c] - dotr) * s.invDr;
+                    int c1 = (c + 1) % 3, c2 = (c + 2) % 3;
+                    gb[c] += gn * (s.z[c1] * s.z[c2]);
+                    gzv[c1] += gn * (s.b[c] * s.z[c2]);
+                    gzv[c2] += gn * (s.b[c] * s.z[c1]);
+                }
+            } else if (settings & ORACLE_UNCLIPPED) {
+                for (int c = 0; c < 3; ++c) gb[c] += gout[c];
             }
             /* b = w / A */
             R gw[3];

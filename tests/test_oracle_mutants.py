@@ -15,6 +15,7 @@ import pytest
 
 import test_oracle_exact as T2
 import test_oracle_fd as T4
+import test_oracle_settings as T5
 from exact_raster import exact_rasterize
 from parity import compare_forward, exact_excuse
 
@@ -40,8 +41,20 @@ MUTANTS = [
     ("bwd_clip_gate_dropped", "(s.b[c] > (R)0 && s.b[c] < (R)1) ? gc : (R)0", "gc"),
     ("bwd_dist_weight", "R ga = gd2 * (R)-2 * ((R)1 - t);", "R ga = gd2 * (R)-2 * t;"),
     ("bwd_inside_sign", "R gd2 = s.inside ? -gd : gd;", "R gd2 = gd;"),
-    ("bwd_renorm_dot_dropped", "R gc = (gbh[c] - dot) * s.invS;", "R gc = gbh[c] * s.invS;"),
+    ("bwd_renorm_dot_dropped", "gc = (gbh[c] - dot) * s.invS;", "gc = gbh[c] * s.invS;"),
     ("bwd_depth_grad", "gzv[c] = gz * s.bh[c];", "gzv[c] = gz * s.c[c];"),
+    # settings (perspective-correct, back-face culling, unclipped barycentrics)
+    ("persp_weight_index", "s->n[k] = (s->c[k] * s->z[(k + 1) % 3]) * s->z[(k + 2) % 3];",
+     "s->n[k] = (s->c[k] * s->z[k]) * s->z[(k + 2) % 3];"),
+    ("persp_depth_guard_dropped",
+     "if ((settings & ORACLE_PERSPECTIVE) && !(s->z[0] > (R)0 && s->z[1] > (R)0 && s->z[2] > (R)0)) return 0;", ""),
+    ("cull_sign", "(settings & ORACLE_CULL_BACK) && s->A > (R)0", "(settings & ORACLE_CULL_BACK) && s->A < (R)0"),
+    ("raw_persp_from_clipped", "s->nr[k] = (s->b[k] * s->z[(k + 1) % 3])", "s->nr[k] = (s->c[k] * s->z[(k + 1) % 3])"),
+    ("raw_returns_clipped", "for (int k = 0; k < 3; ++k) s->out[k] = s->b[k];", ""),
+    ("bwd_persp_dot_dropped", "R gn = (gbh[c] - dot) * s.invD;", "R gn = gbh[c] * s.invD;"),
+    ("bwd_persp_dz_index", "gzv[c1] += gn * (s.c[c] * s.z[c2]);", "gzv[c1] += gn * (s.c[c] * s.z[c1]);"),
+    ("bwd_raw_grad_dropped", "for (int c = 0; c < 3; ++c) gb[c] += gout[c];", ""),
+    ("bwd_raw_persp_dz_index", "gzv[c2] += gn * (s.b[c] * s.z[c1]);", "gzv[c2] += gn * (s.b[c] * s.z[c2]);"),
 ]
 
 
@@ -119,9 +132,41 @@ def _fd_ok(oracle, lib):
     return True
 
 
+class _Bound:
+    """The oracle module with its calls directed to one built library."""
+
+    def __init__(self, oracle, lib):
+        self._oracle, self._lib = oracle, lib
+
+    def rasterize(self, *args, **kw):
+        return self._oracle.rasterize(*args, lib_path=self._lib, **kw)
+
+    def backward(self, *args, **kw):
+        return self._oracle.backward(*args, lib_path=self._lib, **kw)
+
+
+def _settings_ok(oracle, lib):
+    b = _Bound(oracle, lib)
+    checks = [lambda: T5.test_perspective_matches_reciprocal_form(b, 0),
+              lambda: T5.test_perspective_skips_faces_behind_the_camera(b),
+              lambda: T5.test_culling_equals_degenerate_back_faces(b, 3),
+              lambda: T5.test_culling_keeps_the_first_hit_of_closed_meshes(b),
+              lambda: T5.test_unclipped_barycentrics(b, 5)]
+    for name in T5.SETTINGS:
+        for seed in range(4):
+            checks.append(lambda name=name, seed=seed: T5.test_backward_matches_finite_differences(b, name, seed))
+    for check in checks:
+        try:
+            check()
+        except AssertionError:
+            return False
+    return True
+
+
 def test_unmutated_copy_passes(oracle_mod, tmp_path):
     lib = oracle_mod.build(out_path=str(tmp_path / "lib.so"))
     assert _golden_ok(oracle_mod, lib) and _exact_ok(oracle_mod, lib) and _fd_ok(oracle_mod, lib)
+    assert _settings_ok(oracle_mod, lib)
 
 
 @pytest.mark.parametrize("mutant", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -134,5 +179,6 @@ def test_planted_mistake_is_caught(oracle_mod, tmp_path, mutant):
     assert src.count(old) == 1, f"mutation site for {name} not found exactly once"
     impl.write_text(src.replace(old, new))
     lib = oracle_mod.build(out_path=str(tmp_path / "lib.so"), source_dir=str(tmp_path))
-    caught = (not _golden_ok(oracle_mod, lib)) or (not _exact_ok(oracle_mod, lib)) or (not _fd_ok(oracle_mod, lib))
+    caught = ((not _golden_ok(oracle_mod, lib)) or (not _exact_ok(oracle_mod, lib)) or (not _fd_ok(oracle_mod, lib))
+              or (not _settings_ok(oracle_mod, lib)))
     assert caught, f"planted mistake {name} passed every pin"
