@@ -7,6 +7,8 @@ computation runs in the library's HIP kernels. There is no CPU fallback: if
 libdmr.so is missing, every call raises.
 
     rasterize_meshes_fwd / rasterize_meshes_bwd   the two C-ABI entry points
+    rasterize_meshes_fwd_ex                       the forward with rasterizer settings
+    dmr_blend_fwd / dmr_blend_bwd                 the second stage
     rasterize_meshes                              autograd-aware convenience
 """
 
@@ -23,10 +25,13 @@ LIB_PATH = os.path.join(_HERE, "libdmr.so")
 
 DMR_MAX_K = 64
 DMR_BWD_REUSE_FORWARD_WORKSPACE = 0x1
+DMR_RASTER_PERSPECTIVE_CORRECT = 0x2
+DMR_RASTER_CULL_BACKFACES = 0x4
+DMR_RASTER_UNCLIPPED_BARY = 0x8
 STATUS = {0: "DMR_SUCCESS", 1: "DMR_ERROR_INVALID_VALUE", 2: "DMR_ERROR_WORKSPACE_TOO_SMALL",
           3: "DMR_ERROR_HIP", 4: "DMR_ERROR_UNSUPPORTED"}
 EXPORTED = [
-    "rasterize_meshes_fwd", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
+    "rasterize_meshes_fwd", "rasterize_meshes_fwd_ex", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
     "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
     "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd",
@@ -67,6 +72,9 @@ def lib(path: Optional[str] = None):
     L.rasterize_meshes_fwd.restype = ctypes.c_int
     L.rasterize_meshes_fwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
                                        P, P, P, P, P, SZ, P]
+    L.rasterize_meshes_fwd_ex.restype = ctypes.c_int
+    L.rasterize_meshes_fwd_ex.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
+                                          P, P, P, P, P, SZ, ctypes.c_uint32, P]
     L.rasterize_meshes_bwd.restype = ctypes.c_int
     L.rasterize_meshes_bwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P, SZ,
                                        ctypes.c_uint32, P]
@@ -159,6 +167,22 @@ def rasterize_meshes_fwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
                          pix_to_face: torch.Tensor, zbuf: torch.Tensor, bary: torch.Tensor,
                          dists: torch.Tensor, workspace: torch.Tensor) -> None:
     """C-ABI forward call on preallocated device tensors (include/dmr.h)."""
+    _forward(verts, faces, mesh_face_offsets, H, W, K, blur_radius, pix_to_face, zbuf, bary, dists, workspace,
+             None)
+
+
+def rasterize_meshes_fwd_ex(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
+                            H: int, W: int, K: int, blur_radius: float,
+                            pix_to_face: torch.Tensor, zbuf: torch.Tensor, bary: torch.Tensor,
+                            dists: torch.Tensor, workspace: torch.Tensor, flags: int) -> None:
+    """C-ABI forward call with rasterizer settings (a mask of the
+    DMR_RASTER_* bits; include/dmr.h)."""
+    _forward(verts, faces, mesh_face_offsets, H, W, K, blur_radius, pix_to_face, zbuf, bary, dists, workspace,
+             int(flags))
+
+
+def _forward(verts, faces, mesh_face_offsets, H, W, K, blur_radius, pix_to_face, zbuf, bary, dists, workspace,
+             flags):
     dev = verts.device
     N = mesh_face_offsets.shape[0] - 1
     _check(verts, "verts", torch.float32, dev)
@@ -170,23 +194,30 @@ def rasterize_meshes_fwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
     _check(bary, "bary", torch.float32, dev, shape + (3,))
     _check(dists, "dists", torch.float32, dev, shape)
     _check(workspace, "workspace", torch.uint8, dev)
-    rc = lib().rasterize_meshes_fwd(
-        _ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
-        H, W, K, float(blur_radius), _ptr(pix_to_face), _ptr(zbuf), _ptr(bary), _ptr(dists),
-        _ptr(workspace), workspace.numel(), _stream_handle(dev))
-    if rc != 0:
-        raise DmrError("rasterize_meshes_fwd", rc)
+    args = (_ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
+            H, W, K, float(blur_radius), _ptr(pix_to_face), _ptr(zbuf), _ptr(bary), _ptr(dists),
+            _ptr(workspace), workspace.numel())
+    if flags is None:
+        rc = lib().rasterize_meshes_fwd(*args, _stream_handle(dev))
+        if rc != 0:
+            raise DmrError("rasterize_meshes_fwd", rc)
+    else:
+        rc = lib().rasterize_meshes_fwd_ex(*args, flags, _stream_handle(dev))
+        if rc != 0:
+            raise DmrError("rasterize_meshes_fwd_ex", rc)
 
 
 def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
                          H: int, W: int, K: int, blur_radius: float, pix_to_face: torch.Tensor,
                          grad_zbuf: Optional[torch.Tensor], grad_bary: Optional[torch.Tensor],
                          grad_dists: Optional[torch.Tensor], grad_verts: torch.Tensor,
-                         workspace: Optional[torch.Tensor] = None, reuse_forward_workspace: bool = False) -> None:
+                         workspace: Optional[torch.Tensor] = None, reuse_forward_workspace: bool = False,
+                         settings: int = 0) -> None:
     """C-ABI backward call on preallocated device tensors (include/dmr.h).
 
     With reuse_forward_workspace=True, `workspace` must be the forward call's
-    workspace for these same inputs, unmodified since."""
+    workspace for these same inputs, unmodified since. `settings` are the
+    DMR_RASTER_* bits the forward call was given."""
     dev = verts.device
     N = mesh_face_offsets.shape[0] - 1
     shape = (N, H, W, K)
@@ -199,7 +230,7 @@ def rasterize_meshes_bwd(verts: torch.Tensor, faces: torch.Tensor, mesh_face_off
     _check(grad_dists, "grad_dists", torch.float32, dev, shape, optional=True)
     _check(grad_verts, "grad_verts", torch.float32, dev, tuple(verts.shape))
     _check(workspace, "workspace", torch.uint8, dev, optional=not reuse_forward_workspace)
-    flags = DMR_BWD_REUSE_FORWARD_WORKSPACE if reuse_forward_workspace else 0
+    flags = (DMR_BWD_REUSE_FORWARD_WORKSPACE if reuse_forward_workspace else 0) | int(settings)
     rc = lib().rasterize_meshes_bwd(
         _ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0], _ptr(mesh_face_offsets), N,
         H, W, K, float(blur_radius), _ptr(pix_to_face), _ptr(grad_zbuf), _ptr(grad_bary), _ptr(grad_dists),
@@ -297,43 +328,49 @@ def _alloc_outputs(N, H, W, K, device):
 
 class _RasterizeMeshes(torch.autograd.Function):
     @staticmethod
-    def forward(ctx, verts, faces, offsets, H, W, K, blur_radius):
+    def forward(ctx, verts, faces, offsets, H, W, K, blur_radius, settings):
         N = offsets.shape[0] - 1
         out = _alloc_outputs(N, H, W, K, verts.device)
         # Each call owns its workspace: the backward pass reuses its face
         # records and bin lists, so it must survive until then.
         ws = torch.empty(dmr_workspace_size_hint(N, faces.shape[0], H, W, K, blur_radius), dtype=torch.uint8,
                          device=verts.device)
-        rasterize_meshes_fwd(verts, faces, offsets, H, W, K, blur_radius, *out, ws)
+        rasterize_meshes_fwd_ex(verts, faces, offsets, H, W, K, blur_radius, *out, ws, settings)
         ctx.save_for_backward(verts, faces, offsets, out[0], ws)
-        ctx.dims = (H, W, K, blur_radius)
+        ctx.dims = (H, W, K, blur_radius, settings)
         ctx.mark_non_differentiable(out[0])
         return out
 
     @staticmethod
     def backward(ctx, g_p2f, g_zbuf, g_bary, g_dists):
         verts, faces, offsets, p2f, ws = ctx.saved_tensors
-        H, W, K, blur_radius = ctx.dims
+        H, W, K, blur_radius, settings = ctx.dims
         grad_verts = torch.empty_like(verts)
 
         def c(g):
             return None if g is None else g.contiguous()
 
         rasterize_meshes_bwd(verts, faces, offsets, H, W, K, blur_radius, p2f, c(g_zbuf), c(g_bary), c(g_dists),
-                             grad_verts, ws, reuse_forward_workspace=True)
-        return grad_verts, None, None, None, None, None, None
+                             grad_verts, ws, reuse_forward_workspace=True, settings=settings)
+        return grad_verts, None, None, None, None, None, None, None
 
 
 def rasterize_meshes(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
-                     image_size: Tuple[int, int], faces_per_pixel: int = 1, blur_radius: float = 0.0):
+                     image_size: Tuple[int, int], faces_per_pixel: int = 1, blur_radius: float = 0.0,
+                     perspective_correct: bool = False, cull_backfaces: bool = False,
+                     clip_barycentric_coords: bool = True):
     """Rasterizes a packed batch of meshes on the GPU.
 
     verts [V,3] float32 (x, y NDC, z depth), faces [F,3] int64, mesh_face_offsets
     [N+1] int64. Returns (pix_to_face, zbuf, bary, dists); zbuf, bary and dists
-    are differentiable with respect to verts."""
+    are differentiable with respect to verts. The three settings map to the
+    DMR_RASTER_* bits of include/dmr.h."""
     H, W = image_size
+    settings = ((DMR_RASTER_PERSPECTIVE_CORRECT if perspective_correct else 0)
+                | (DMR_RASTER_CULL_BACKFACES if cull_backfaces else 0)
+                | (0 if clip_barycentric_coords else DMR_RASTER_UNCLIPPED_BARY))
     return _RasterizeMeshes.apply(verts, faces, mesh_face_offsets, int(H), int(W), int(faces_per_pixel),
-                                  float(blur_radius))
+                                  float(blur_radius), settings)
 
 
 # ----------------------------------------------------------------------------

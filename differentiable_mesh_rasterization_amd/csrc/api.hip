@@ -150,10 +150,20 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
                                 const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
                                 float blur_radius, int64_t* pix_to_face, float* zbuf, float* bary,
                                 float* dists, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    return rasterize_meshes_fwd_ex(verts, V, faces, F, mesh_face_offsets, N, H, W, K, blur_radius, pix_to_face, zbuf,
+                                   bary, dists, workspace, workspace_bytes, 0u, stream);
+}
+
+dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                   const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
+                                   float blur_radius, int64_t* pix_to_face, float* zbuf, float* bary,
+                                   float* dists, void* workspace, size_t workspace_bytes, uint32_t flags,
+                                   hipStream_t stream) {
     int64_t slots = 0;
     dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
     if (st != DMR_SUCCESS) return st;
     if (!isfinite(blur_radius) || blur_radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
+    if ((flags & ~(uint32_t)DMR_RASTER_SETTINGS) != 0) return DMR_ERROR_INVALID_VALUE;
     if (slots == 0) return DMR_SUCCESS;
     if (!pix_to_face || !zbuf || !bary || !dists) return DMR_ERROR_INVALID_VALUE;
     FwdLayout L = fwd_layout(N, F, H, W);
@@ -165,7 +175,7 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
 
     FwdArgs a;
     a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
-    a.H = H; a.W = W; a.K = K; a.blur = blur_radius;
+    a.H = H; a.W = W; a.K = K; a.blur = blur_radius; a.settings = flags;
     a.pix_to_face = pix_to_face; a.zbuf = zbuf; a.bary = bary; a.dists = dists;
     a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes;
     a.L = L; a.capacity = cap; a.stream = stream;
@@ -181,7 +191,8 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
     dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
     if (st != DMR_SUCCESS) return st;
     if (!isfinite(blur_radius) || blur_radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
-    if ((flags & ~(uint32_t)DMR_BWD_REUSE_FORWARD_WORKSPACE) != 0) return DMR_ERROR_INVALID_VALUE;
+    if ((flags & ~(uint32_t)(DMR_BWD_REUSE_FORWARD_WORKSPACE | DMR_RASTER_SETTINGS)) != 0)
+        return DMR_ERROR_INVALID_VALUE;
     if (V > 0 && grad_verts == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (slots > 0 && pix_to_face == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (V == 0) return DMR_SUCCESS;
@@ -194,7 +205,8 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
     if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
     BwdArgs a;
     a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
-    a.H = H; a.W = W; a.K = K; a.blur = blur_radius; a.pix_to_face = pix_to_face;
+    a.H = H; a.W = W; a.K = K; a.blur = blur_radius; a.settings = flags & DMR_RASTER_SETTINGS;
+    a.pix_to_face = pix_to_face;
     a.gz = grad_zbuf; a.gb = grad_bary; a.gd = grad_dists; a.grad_verts = grad_verts;
     a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes; a.L = L; a.capacity = cap;
     a.reuse_forward = reuse;

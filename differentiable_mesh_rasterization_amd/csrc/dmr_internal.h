@@ -124,18 +124,31 @@ __device__ __forceinline__ float pixel_centre(int j, int W) {
 
 // Full evaluation of one (pixel, face) pair, mirroring the conventions
 // operation by operation. `want_dist` forces the distance even when the
-// pixel is inside (needed for the dists output).
+// pixel is inside (needed for the dists output); `settings` holds the
+// DMR_RASTER_* bits of include/dmr.h.
 struct PairState {
     float b0, b1, b2;      // raw barycentrics
     bool inside;
     float d2;              // squared distance to the nearest edge (if computed)
     int argmin;            // nearest edge (first minimum)
     float t, rx, ry;       // its clamp parameter and residual
-    float c0, c1, c2, invS;
-    float bh0, bh1, bh2;   // clipped, renormalised barycentrics
+    float c0, c1, c2;      // clipped barycentrics
+    float invS;            // 1 / (c0 + c1 + c2), or with perspective 1 / (n0 + n1 + n2)
+    float bh0, bh1, bh2;   // normalised (and perspective-weighted) clipped barycentrics
     float z;               // depth at the pixel
     bool cand;             // included and z > 0
+    float o0, o1, o2;      // the returned barycentrics
+    float invDr;           // unclipped with perspective: 1 / (nr0 + nr1 + nr2)
 };
+
+// Perspective weights of barycentrics a at vertex depths z: n_k = (a_k
+// z_{k+1}) z_{k+2}, i.e. a_k / z_k scaled by z0 z1 z2.
+__device__ __forceinline__ void persp_weights(float a0, float a1, float a2, float z0, float z1, float z2, float& n0,
+                                              float& n1, float& n2) {
+    n0 = (a0 * z1) * z2;
+    n1 = (a1 * z2) * z0;
+    n2 = (a2 * z0) * z1;
+}
 
 __device__ __forceinline__ void edge_distance(float px, float py, float ax, float ay, float bx, float by,
                                               float il, float& d, float& t, float& rx, float& ry) {
@@ -152,7 +165,7 @@ __device__ __forceinline__ void edge_distance(float px, float py, float ax, floa
 }
 
 __device__ __forceinline__ void eval_pair(const FaceRec& r, float px, float py, float blur, bool want_dist,
-                                          PairState& s) {
+                                          uint32_t settings, PairState& s) {
     float dx0 = r.x0 - px, dy0 = r.y0 - py;
     float dx1 = r.x1 - px, dy1 = r.y1 - py;
     float dx2 = r.x2 - px, dy2 = r.y2 - py;
@@ -189,13 +202,37 @@ __device__ __forceinline__ void eval_pair(const FaceRec& r, float px, float py, 
     c1 = c1 > 1.0f ? 1.0f : c1;
     c2 = c2 > 1.0f ? 1.0f : c2;
     s.c0 = c0; s.c1 = c1; s.c2 = c2;
-    float S = (c0 + c1) + c2;
-    s.invS = 1.0f / S;
-    s.bh0 = c0 * s.invS;
-    s.bh1 = c1 * s.invS;
-    s.bh2 = c2 * s.invS;
+    const bool persp = (settings & DMR_RASTER_PERSPECTIVE_CORRECT) != 0;
+    if (persp) {
+        float n0, n1, n2;
+        persp_weights(c0, c1, c2, r.z0, r.z1, r.z2, n0, n1, n2);
+        s.invS = 1.0f / ((n0 + n1) + n2);
+        s.bh0 = n0 * s.invS;
+        s.bh1 = n1 * s.invS;
+        s.bh2 = n2 * s.invS;
+    } else {
+        float S = (c0 + c1) + c2;
+        s.invS = 1.0f / S;
+        s.bh0 = c0 * s.invS;
+        s.bh1 = c1 * s.invS;
+        s.bh2 = c2 * s.invS;
+    }
     s.z = (s.bh0 * r.z0 + s.bh1 * r.z1) + s.bh2 * r.z2;
     s.cand = s.z > 0.0f;
+    s.o0 = s.bh0; s.o1 = s.bh1; s.o2 = s.bh2;
+    s.invDr = 0.0f;
+    if (settings & DMR_RASTER_UNCLIPPED_BARY) {
+        if (persp) {
+            float n0, n1, n2;
+            persp_weights(s.b0, s.b1, s.b2, r.z0, r.z1, r.z2, n0, n1, n2);
+            s.invDr = 1.0f / ((n0 + n1) + n2);
+            s.o0 = n0 * s.invDr;
+            s.o1 = n1 * s.invDr;
+            s.o2 = n2 * s.invDr;
+        } else {
+            s.o0 = s.b0; s.o1 = s.b1; s.o2 = s.b2;
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -221,6 +258,7 @@ struct FwdArgs {
     const int64_t* off; int64_t N;
     int32_t H, W, K;
     float blur;
+    uint32_t settings;     // DMR_RASTER_* bits
     int64_t* pix_to_face; float* zbuf; float* bary; float* dists;
     char* ws; size_t ws_bytes;
     FwdLayout L;
@@ -234,6 +272,7 @@ struct BwdArgs {
     const int64_t* off; int64_t N;
     int32_t H, W, K;
     float blur;
+    uint32_t settings;     // DMR_RASTER_* bits
     const int64_t* pix_to_face;
     const float* gz; const float* gb; const float* gd;
     float* grad_verts;

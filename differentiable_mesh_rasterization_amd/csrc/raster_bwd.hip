@@ -6,8 +6,10 @@
 // of each pixel's list) are compacted into an LDS list, so that every lane
 // works on a real (pixel, face) pair. Each pair re-runs the forward
 // evaluation and applies the chain rule of zbuf = sum bh_k z_k,
-// bh = clip(b)/S, b = w/A and dists = +-|q - t u|^2 (t held at its
-// minimiser or clamp). The nine partials are summed per vertex in an LDS
+// bh = clip(b)/S (with perspective correction bh = n/D, n_k = c_k z_{k+1}
+// z_{k+2}), b = w/A and dists = +-|q - t u|^2 (t held at its minimiser or
+// clamp); the returned barycentrics are bh, or the unclipped b (perspective-
+// weighted the same way) on request. The nine partials are summed per vertex in an LDS
 // hash table, then flushed into grad_verts with one float32 global atomic
 // per (tile, vertex, coordinate).
 //
@@ -53,20 +55,62 @@ __device__ __forceinline__ void load_face(const float* __restrict__ verts, const
     r.ymax = fmaxf(r.y0, fmaxf(r.y1, r.y2));
 }
 
+// Backward of the perspective weighting o = n / D, n_k = a_k z_{k+1} z_{k+2}
+// (a: the weighted barycentrics, inv_d = 1 / D): adds dL/da to ga and the
+// depth partials to gzv, from the gradient go of o.
+__device__ __forceinline__ void persp_backward(float go0, float go1, float go2, float o0, float o1, float o2,
+                                               float inv_d, float a0, float a1, float a2, const FaceRec& r,
+                                               float& ga0, float& ga1, float& ga2, float& gzv0, float& gzv1,
+                                               float& gzv2) {
+    const float dot = (go0 * o0 + go1 * o1) + go2 * o2;
+    const float gn0 = (go0 - dot) * inv_d, gn1 = (go1 - dot) * inv_d, gn2 = (go2 - dot) * inv_d;
+    ga0 += gn0 * (r.z1 * r.z2);
+    ga1 += gn1 * (r.z2 * r.z0);
+    ga2 += gn2 * (r.z0 * r.z1);
+    gzv1 += gn0 * (a0 * r.z2);
+    gzv2 += gn0 * (a0 * r.z1);
+    gzv2 += gn1 * (a1 * r.z0);
+    gzv0 += gn1 * (a1 * r.z2);
+    gzv0 += gn2 * (a2 * r.z1);
+    gzv1 += gn2 * (a2 * r.z0);
+}
+
 // Per-slot chain rule. Returns the nine partials (x, y, z of the three
-// vertices) of L = gz*zbuf + gb.bary + gd*dists for one filled slot.
+// vertices) of L = gz*zbuf + gb.bary + gd*dists for one filled slot; `gout`
+// is the gradient of the returned barycentrics.
 __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState& s, float px, float py, float gz,
-                                              float gbh0, float gbh1, float gbh2, float gd, float (&g)[9]) {
+                                              float gout0, float gout1, float gout2, float gd, uint32_t settings,
+                                              float (&g)[9]) {
+    const bool persp = (settings & DMR_RASTER_PERSPECTIVE_CORRECT) != 0;
+    const bool unclipped = (settings & DMR_RASTER_UNCLIPPED_BARY) != 0;
     // depth
-    const float gzv0 = gz * s.bh0, gzv1 = gz * s.bh1, gzv2 = gz * s.bh2;
-    gbh0 = gbh0 + gz * r.z0;
-    gbh1 = gbh1 + gz * r.z1;
-    gbh2 = gbh2 + gz * r.z2;
-    // renormalisation and clip
-    const float dot = (gbh0 * s.bh0 + gbh1 * s.bh1) + gbh2 * s.bh2;
-    const float gb0 = (s.b0 > 0.0f && s.b0 < 1.0f) ? (gbh0 - dot) * s.invS : 0.0f;
-    const float gb1 = (s.b1 > 0.0f && s.b1 < 1.0f) ? (gbh1 - dot) * s.invS : 0.0f;
-    const float gb2 = (s.b2 > 0.0f && s.b2 < 1.0f) ? (gbh2 - dot) * s.invS : 0.0f;
+    float gzv0 = gz * s.bh0, gzv1 = gz * s.bh1, gzv2 = gz * s.bh2;
+    float gbh0 = (unclipped ? 0.0f : gout0) + gz * r.z0;
+    float gbh1 = (unclipped ? 0.0f : gout1) + gz * r.z1;
+    float gbh2 = (unclipped ? 0.0f : gout2) + gz * r.z2;
+    // normalisation (or perspective weighting) and clip
+    float gc0 = 0.0f, gc1 = 0.0f, gc2 = 0.0f;
+    if (persp) {
+        persp_backward(gbh0, gbh1, gbh2, s.bh0, s.bh1, s.bh2, s.invS, s.c0, s.c1, s.c2, r, gc0, gc1, gc2, gzv0, gzv1,
+                       gzv2);
+    } else {
+        const float dot = (gbh0 * s.bh0 + gbh1 * s.bh1) + gbh2 * s.bh2;
+        gc0 = (gbh0 - dot) * s.invS;
+        gc1 = (gbh1 - dot) * s.invS;
+        gc2 = (gbh2 - dot) * s.invS;
+    }
+    float gb0 = (s.b0 > 0.0f && s.b0 < 1.0f) ? gc0 : 0.0f;
+    float gb1 = (s.b1 > 0.0f && s.b1 < 1.0f) ? gc1 : 0.0f;
+    float gb2 = (s.b2 > 0.0f && s.b2 < 1.0f) ? gc2 : 0.0f;
+    // unclipped barycentrics returned: their gradient reaches b directly
+    if (unclipped && persp) {
+        persp_backward(gout0, gout1, gout2, s.o0, s.o1, s.o2, s.invDr, s.b0, s.b1, s.b2, r, gb0, gb1, gb2, gzv0, gzv1,
+                       gzv2);
+    } else if (unclipped) {
+        gb0 += gout0;
+        gb1 += gout1;
+        gb2 += gout2;
+    }
     // b = w / A
     const float gw0 = gb0 * r.invA, gw1 = gb1 * r.invA, gw2 = gb2 * r.invA;
     const float gA = -((gb0 * s.b0 + gb1 * s.b1) + gb2 * s.b2) * r.invA;
@@ -180,7 +224,11 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& t
 // Tiles come from the grid (one workgroup per tile) or, with the forward's
 // workspace, from a queue in the forward's heaviest-first bin order: each
 // workgroup takes tiles until it meets a bin without faces (those come last
-// and have no filled slot) or the end of the order.
+// and have no filled slot) or the end of the order. SETTINGS holds the
+// DMR_RASTER_* bits that change the per-slot evaluation (perspective
+// correction, unclipped barycentrics), fixed at compile time so that each
+// variant carries only its own arithmetic.
+template <uint32_t SETTINGS>
 __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const FaceRec* __restrict__ recs, const int32_t* __restrict__ bin_order, const int32_t* __restrict__ bin_count,
     int32_t* __restrict__ queue, int64_t bins, const float* __restrict__ verts,
@@ -265,14 +313,14 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
             const float px = pixel_centre(gj, W), py = pixel_centre(gi, H);
             const int64_t so = (((int64_t)n * H + gi) * W + gj) * K + slot;
             PairState s;
-            eval_pair(r, px, py, __builtin_inff(), true, s);
+            eval_pair(r, px, py, __builtin_inff(), true, SETTINGS, s);
             const float gz = gzb ? gzb[so] : 0.0f;
             const float gd = gds ? gds[so] : 0.0f;
             const float gb0 = gba ? gba[3 * so + 0] : 0.0f;
             const float gb1 = gba ? gba[3 * so + 1] : 0.0f;
             const float gb2 = gba ? gba[3 * so + 2] : 0.0f;
             float g[9];
-            slot_partials(r, s, px, py, gz, gb0, gb1, gb2, gd, g);
+            slot_partials(r, s, px, py, gz, gb0, gb1, gb2, gd, SETTINGS, g);
             vertex_add(hkey, hval, grad_verts, vi[0], g[0], g[1], g[2], use_hash);
             vertex_add(hkey, hval, grad_verts, vi[1], g[3], g[4], g[5], use_hash);
             vertex_add(hkey, hval, grad_verts, vi[2], g[6], g[7], g[8], use_hash);
@@ -289,6 +337,29 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     }
     __syncthreads();   // the table is cleared for the next tile
     }
+}
+
+template <uint32_t SETTINGS>
+static void launch_backward_slots(const BwdArgs& a, bool reuse, const FaceRec* recs, const int32_t* order,
+                                  const int32_t* count, int32_t* queue) {
+    int64_t grid = a.L.bins;
+    if (reuse) {
+        // as many workgroups as stay resident; each takes tiles from the queue
+        static int resident_per_cu = 0;
+        int dev = 0, cus = 0;
+        if (resident_per_cu == 0 &&
+            hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident_per_cu, backward_slots<SETTINGS>, kBwdThreads,
+                                                         0) != hipSuccess)
+            resident_per_cu = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            cus = 0;
+        const int64_t resident = (int64_t)std::max(1, cus) * std::max(1, resident_per_cu);
+        grid = std::min<int64_t>(grid, resident);
+    }
+    backward_slots<SETTINGS><<<(unsigned)grid, kBwdThreads, 0, a.stream>>>(
+        recs, order, count, queue, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
+        (int32_t)a.L.nby, a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
 }
 
 hipError_t launch_backward(const BwdArgs& a) {
@@ -310,25 +381,14 @@ hipError_t launch_backward(const BwdArgs& a) {
     const FaceRec* recs = reuse ? reinterpret_cast<const FaceRec*>(a.ws + a.L.off_records) : nullptr;
     const int32_t* order = reuse ? reinterpret_cast<const int32_t*>(a.ws + a.L.off_perm) : nullptr;
     const int32_t* count = reuse ? reinterpret_cast<const int32_t*>(a.ws + a.L.off_count) : nullptr;
-    int64_t grid = a.L.bins;
-    if (reuse) {
-        // as many workgroups as stay resident; each takes tiles from the queue
-        static int resident_per_cu = 0;
-        int dev = 0, cus = 0;
-        if (resident_per_cu == 0 &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident_per_cu, backward_slots, kBwdThreads, 0) !=
-                hipSuccess)
-            resident_per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-        const int64_t resident = (int64_t)std::max(1, cus) * std::max(1, resident_per_cu);
-        grid = std::min<int64_t>(grid, resident);
-    }
+    constexpr uint32_t kP = DMR_RASTER_PERSPECTIVE_CORRECT, kU = DMR_RASTER_UNCLIPPED_BARY;
     timing_begin(kKBackward, a.stream);
-    backward_slots<<<(unsigned)grid, kBwdThreads, 0, a.stream>>>(
-        recs, order, count, queue, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
-        (int32_t)a.L.nby, a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
+    switch (a.settings & (kP | kU)) {
+        case 0: launch_backward_slots<0>(a, reuse, recs, order, count, queue); break;
+        case kP: launch_backward_slots<kP>(a, reuse, recs, order, count, queue); break;
+        case kU: launch_backward_slots<kU>(a, reuse, recs, order, count, queue); break;
+        default: launch_backward_slots<kP | kU>(a, reuse, recs, order, count, queue); break;
+    }
     timing_end(kKBackward, a.stream);
     return hipGetLastError();
 }

@@ -47,7 +47,7 @@ __device__ __forceinline__ int64_t mesh_of(const int64_t* __restrict__ off, int6
 
 __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     const float* __restrict__ verts, int64_t V, const int64_t* __restrict__ faces, int64_t F,
-    const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W, float blur,
+    const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W, float blur, uint32_t settings,
     int32_t nbx, int32_t nby, FaceRec* __restrict__ recs, FaceBin* __restrict__ fbin,
     int32_t* __restrict__ bin_count, int32_t* __restrict__ block_live, WsHeader* __restrict__ hdr) {
     __shared__ int32_t hist[kHistBins];
@@ -99,8 +99,11 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         }
         float A = (x1 - x0) * (y2 - y0) - (y1 - y0) * (x2 - x0);
         // All depths <= 0 means z <= 0 at every pixel: the interpolation
-        // weights are >= 0, so each product and each sum stays <= 0.
+        // weights are >= 0, so each product and each sum stays <= 0. With
+        // perspective correction every depth must be > 0. Back faces (A > 0:
+        // the normal's depth component is positive) are dropped on request.
         bool zpos = (z0 > 0.0f) || (z1 > 0.0f) || (z2 > 0.0f);
+        if (settings & DMR_RASTER_PERSPECTIVE_CORRECT) zpos = (z0 > 0.0f) && (z1 > 0.0f) && (z2 > 0.0f);
         r.x0 = x0; r.y0 = y0; r.x1 = x1; r.y1 = y1; r.x2 = x2; r.y2 = y2;
         r.z0 = z0; r.z1 = z1; r.z2 = z2;
         r.invA = 1.0f / A;
@@ -115,7 +118,8 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         float xmin = fminf(x0, fminf(x1, x2)), xmax = fmaxf(x0, fmaxf(x1, x2));
         float ymin = fminf(y0, fminf(y1, y2)), ymax = fmaxf(y0, fmaxf(y1, y2));
         r.xmin = xmin; r.xmax = xmax; r.ymin = ymin; r.ymax = ymax;
-        if (ok && idx_ok && A != 0.0f && zpos) {
+        const bool back = (settings & DMR_RASTER_CULL_BACKFACES) && A > 0.0f;
+        if (ok && idx_ok && A != 0.0f && zpos && !back) {
             // Conservative pixel box: the face's box grown by the blur radius
             // and by a margin far above the rounding of the inclusion tests.
             float rb = sqrtf(blur);
@@ -550,6 +554,7 @@ __device__ __forceinline__ float edge_dist2(float dxa, float dya, float ux, floa
 // depth (and so the key) is formed before the distance: a pair whose key
 // cannot enter the list is dropped without its three edge distances. The
 // result equals testing inclusion first.
+template <bool PERSP>
 __device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float py, float blur, uint64_t last,
                                               uint64_t& kk) {
     const float dx0 = r.x0 - px, dy0 = r.y0 - py;
@@ -568,9 +573,17 @@ __device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float 
     c0 = c0 > 1.0f ? 1.0f : c0;
     c1 = c1 > 1.0f ? 1.0f : c1;
     c2 = c2 > 1.0f ? 1.0f : c2;
-    const float S = (c0 + c1) + c2;
-    const float invS = 1.0f / S;
-    const float z = ((c0 * invS) * r.z0 + (c1 * invS) * r.z1) + (c2 * invS) * r.z2;
+    float z;
+    if (PERSP) {
+        float n0, n1, n2;
+        persp_weights(c0, c1, c2, r.z0, r.z1, r.z2, n0, n1, n2);
+        const float invD = 1.0f / ((n0 + n1) + n2);
+        z = ((n0 * invD) * r.z0 + (n1 * invD) * r.z1) + (n2 * invD) * r.z2;
+    } else {
+        const float S = (c0 + c1) + c2;
+        const float invS = 1.0f / S;
+        z = ((c0 * invS) * r.z0 + (c1 * invS) * r.z1) + (c2 * invS) * r.z2;
+    }
     if (!(z > 0.0f)) return false;
     kk = ((uint64_t)__float_as_uint(z) << 32) | (uint32_t)r.face;
     if (!(kk < last)) return false;
@@ -628,12 +641,12 @@ __device__ __forceinline__ void merge_with_lane(uint64_t (&key)[KMAX], int mask)
 // The K output slots of each row of the item's region are then written
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
-template <int KMAX>
+template <int KMAX, bool PERSP>
 __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 7 : 1, 8))) void fine_raster(
     const FaceRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t F, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
-    int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, int32_t nbx, int32_t nby,
+    int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, uint32_t settings, int32_t nbx, int32_t nby,
     int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
     float* __restrict__ dists) {
     __shared__ FaceRec srec[kFineThreads];
@@ -755,7 +768,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                         const uint64_t last = key[KMAX - 1] < bound ? key[KMAX - 1] : bound;
                         if (szlo[u] > __uint_as_float((uint32_t)(last >> 32))) continue;
                         uint64_t kk;
-                        if (candidate_key(srec[u], px, py, blur, last, kk)) topk_insert<KMAX>(key, kk);
+                        if (candidate_key<PERSP>(srec[u], px, py, blur, last, kk)) topk_insert<KMAX>(key, kk);
                     }
                 }
             }
@@ -834,10 +847,10 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 const int32_t face = (int32_t)(kbuf[e] & 0xffffffffull);
                 PairState st;
                 eval_pair(recs[face], pixel_centre(bx * kBin + reg_c + jj, W),
-                          pixel_centre(by * kBin + reg_r + ra + rr, H), blur, true, st);
-                bary[3 * so + 0] = st.bh0;
-                bary[3 * so + 1] = st.bh1;
-                bary[3 * so + 2] = st.bh2;
+                          pixel_centre(by * kBin + reg_r + ra + rr, H), blur, true, settings, st);
+                bary[3 * so + 0] = st.o0;
+                bary[3 * so + 1] = st.o1;
+                bary[3 * so + 2] = st.o2;
                 dists[so] = st.inside ? -st.d2 : st.d2;
             }
             __syncthreads();
@@ -849,9 +862,14 @@ template <int KMAX>
 static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const FaceBin* fbin, const int32_t* count,
                         const int64_t* offset, const uint32_t* items, WsHeader* hdr, const int32_t* entries,
                         const float* round_lb) {
-    fine_raster<KMAX><<<grid, kFineThreads, 0, a.stream>>>(
-        recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
-        (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
+    if (a.settings & DMR_RASTER_PERSPECTIVE_CORRECT)
+        fine_raster<KMAX, true><<<grid, kFineThreads, 0, a.stream>>>(
+            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
+            a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
+    else
+        fine_raster<KMAX, false><<<grid, kFineThreads, 0, a.stream>>>(
+            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
+            a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
 }
 
 hipError_t launch_binning(const FwdArgs& a, bool sort) {
@@ -877,8 +895,8 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     if (a.F > 0) {
         timing_begin(kKFaceSetup, a.stream);
         face_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
-            a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, (int32_t)a.L.nbx, (int32_t)a.L.nby, recs,
-            fbin, count, block_live, hdr);
+            a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, a.settings, (int32_t)a.L.nbx,
+            (int32_t)a.L.nby, recs, fbin, count, block_live, hdr);
         timing_end(kKFaceSetup, a.stream);
     }
     timing_begin(kKBinScan, a.stream);

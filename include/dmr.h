@@ -22,6 +22,20 @@
  *   each pixel keeps its K candidates of smallest (z, global face index);
  *   all decisions and values are binary32, evaluated in one fixed operation
  *   order with no fused multiply-add, so results are reproducible bit for bit.
+ * Rasterizer settings (rocketrecap summary, "32:56 Technical Bug Fix", names
+ * a perspective_correct setting; the pages define none of them), bits of the
+ * `flags` of rasterize_meshes_fwd_ex and rasterize_meshes_bwd:
+ *   DMR_RASTER_PERSPECTIVE_CORRECT  a face is a candidate only if its three
+ *       vertex depths are > 0; the clipped barycentrics c are weighted as
+ *       n_k = (c_k z_{k+1}) z_{k+2} (the inverse depths, scaled), normalised
+ *       by n0 + n1 + n2 in place of c0 + c1 + c2, and z = sum of the weighted
+ *       barycentrics times the vertex depths (1/z linear in screen space);
+ *   DMR_RASTER_CULL_BACKFACES  faces with A > 0 are skipped: A is the depth
+ *       component of the normal (v1 - v0) x (v2 - v0), so their normal points
+ *       away from the viewer;
+ *   DMR_RASTER_UNCLIPPED_BARY  bary returns the barycentrics before clipping
+ *       (perspective-weighted the same way with the setting above); depth,
+ *       inclusion and order do not change.
  *
  * Memory: every pointer argument is a device pointer on the device the
  * stream belongs to (the default device for the null stream); arrays are
@@ -63,6 +77,11 @@ typedef enum dmr_status {
 #define DMR_MAX_IMAGE_SIDE 32767
 #define DMR_FLAG_BAD_VERTEX_INDEX 0x1u
 
+#define DMR_RASTER_PERSPECTIVE_CORRECT 0x2u
+#define DMR_RASTER_CULL_BACKFACES 0x4u
+#define DMR_RASTER_UNCLIPPED_BARY 0x8u
+#define DMR_RASTER_SETTINGS (DMR_RASTER_PERSPECTIVE_CORRECT | DMR_RASTER_CULL_BACKFACES | DMR_RASTER_UNCLIPPED_BARY)
+
 /*
  * Forward pass: K nearest faces per pixel.
  *
@@ -95,6 +114,15 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
                                 int64_t* pix_to_face, float* zbuf, float* bary, float* dists,
                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* The forward pass with rasterizer settings: flags is a mask of the
+ * DMR_RASTER_* bits (any other bit: DMR_ERROR_INVALID_VALUE); flags = 0 is
+ * rasterize_meshes_fwd. A backward pass of its outputs takes the same bits. */
+dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                   const int64_t* mesh_face_offsets, int64_t N,
+                                   int32_t H, int32_t W, int32_t K, float blur_radius,
+                                   int64_t* pix_to_face, float* zbuf, float* bary, float* dists,
+                                   void* workspace, size_t workspace_bytes, uint32_t flags, hipStream_t stream);
+
 /*
  * Backward pass: maps the gradients of zbuf, bary and dists to vertex
  * positions (rocketrecap summary, "3:52 Differentiable Renderer": gradients
@@ -107,8 +135,10 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
  *              upstream gradients; any of them may be NULL (= zero). Values on
  *              padded slots are ignored.
  *   grad_verts [V,3] float32: overwritten (not accumulated) with dL/dverts.
- *   workspace, flags
- *              With flags = DMR_BWD_REUSE_FORWARD_WORKSPACE, `workspace` is the
+ *   flags      the DMR_RASTER_* bits the forward pass was given, plus
+ *              optionally DMR_BWD_REUSE_FORWARD_WORKSPACE (any other bit:
+ *              DMR_ERROR_INVALID_VALUE).
+ *   workspace  With DMR_BWD_REUSE_FORWARD_WORKSPACE, `workspace` is the
  *              forward pass's workspace for these same inputs, unmodified
  *              since that call (workspace_bytes as given to it); its per-face
  *              records replace recomputing each face's data from verts and
@@ -117,7 +147,7 @@ dmr_status rasterize_meshes_fwd(const float* verts, int64_t V, const int64_t* fa
  *              not checked, and any other content gives wrong gradients. The
  *              call writes one counter word of the workspace header (its tile
  *              queue), so backward calls sharing a workspace must not overlap
- *              in time. With flags = 0 the workspace is not used and may be
+ *              in time. Without that bit the workspace is not used and may be
  *              NULL.
  * Contributions are summed per 16x16 tile and vertex in LDS, then added to
  * grad_verts with float32 atomics, so the rounding of grad_verts may differ

@@ -40,7 +40,9 @@ class GpuCase:
     def from_workload(cls, w):
         return cls(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur)
 
-    def forward(self, ws_bytes=None, out=None):
+    def forward(self, ws_bytes=None, out=None, settings=None):
+        """Forward pass (rasterize_meshes_fwd, or rasterize_meshes_fwd_ex
+        with `settings`); the settings are kept for backward()."""
         import differentiable_mesh_rasterization_amd as dmr
 
         N, H, W, K = self.N, self.H, self.W, self.K
@@ -52,9 +54,14 @@ class GpuCase:
         if ws_bytes is None:
             ws_bytes = dmr.dmr_workspace_size_hint(N, self.faces.shape[0], H, W, K, self.blur)
         ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=DEV)
-        dmr.rasterize_meshes_fwd(self.verts, self.faces, self.offsets, H, W, K, self.blur, *out, ws)
+        if settings is None:
+            dmr.rasterize_meshes_fwd(self.verts, self.faces, self.offsets, H, W, K, self.blur, *out, ws)
+        else:
+            dmr.rasterize_meshes_fwd_ex(self.verts, self.faces, self.offsets, H, W, K, self.blur, *out, ws,
+                                        settings)
         torch.cuda.synchronize()
         self.ws = ws
+        self.settings = settings or 0
         return out
 
     def backward(self, p2f, gz=None, gb=None, gd=None, reuse=True):
@@ -65,7 +72,8 @@ class GpuCase:
         gv = torch.empty_like(self.verts)
         ws = self.ws if reuse else None
         dmr.rasterize_meshes_bwd(self.verts, self.faces, self.offsets, self.H, self.W, self.K, self.blur, p2f,
-                                 gz, gb, gd, gv, ws, reuse_forward_workspace=reuse)
+                                 gz, gb, gd, gv, ws, reuse_forward_workspace=reuse,
+                                 settings=getattr(self, "settings", 0))
         torch.cuda.synchronize()
         return gv
 

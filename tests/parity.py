@@ -77,9 +77,10 @@ def _diff_faces(ref_faces, got_faces):
     return out
 
 
-def oracle_excuse(oracle, w_verts, w_faces, w_offsets, H, W, blur, pixel_ids=None, delta=DELTA):
-    """Excuse function backed by the binary32 oracle: pixel rows index
-    pixel_ids (or all pixels in order when pixel_ids is None)."""
+def oracle_excuse(oracle, w_verts, w_faces, w_offsets, H, W, blur, pixel_ids=None, delta=DELTA, settings=0):
+    """Excuse function backed by the binary32 oracle (with the given
+    rasterizer settings): pixel rows index pixel_ids (or all pixels in order
+    when pixel_ids is None)."""
     offsets = np.asarray(w_offsets)
 
     def fn(row, ref_faces, got_faces, ref_z, got_z):
@@ -89,7 +90,7 @@ def oracle_excuse(oracle, w_verts, w_faces, w_offsets, H, W, blur, pixel_ids=Non
         runs = {}
         for tag, b in (("mid", blur), ("lo", max(0.0, blur - delta)), ("hi", blur + delta)):
             p, z, _, _ = oracle.rasterize(w_verts, w_faces, offsets, H, W, Kall, b,
-                                          pixels=np.asarray([pid]))
+                                          pixels=np.asarray([pid]), settings=settings)
             m = p[0] >= 0
             runs[tag] = dict(zip(p[0][m].tolist(), z[0][m].tolist()))
         near_blur = set(runs["hi"]) - set(runs["lo"])

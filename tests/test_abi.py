@@ -104,6 +104,17 @@ def test_forward_rejects_invalid_arguments(dmr, kw, status):
     assert _fwd(dmr.lib(), **kw) == status
 
 
+@pytest.mark.parametrize("flags,status", [(0x1, INVALID), (0x10, INVALID), (0x80000000, INVALID),
+                                          (0xE, WS_SMALL), (0x2, WS_SMALL)])
+def test_forward_ex_checks_its_flags(dmr, flags, status):
+    # valid settings get as far as the workspace check (ws_bytes=100 is too small)
+    L = dmr.lib()
+    fake = ctypes.c_void_p(0x1000)
+    rc = L.rasterize_meshes_fwd_ex(fake, 3, fake, 1, fake, 1, 8, 8, 1, 0.0, fake, fake, fake, fake, fake, 100,
+                                   flags, None)
+    assert rc == status
+
+
 def test_forward_with_nothing_to_draw_is_a_no_op(dmr):
     # N = 0: no pixels; succeeds without reading any pointer or touching the GPU
     assert _fwd(dmr.lib(), N=0, off=None, p2f=None, zbuf=None, bary=None, dists=None, ws=None) == SUCCESS
@@ -113,7 +124,7 @@ def test_forward_with_nothing_to_draw_is_a_no_op(dmr):
 @pytest.mark.parametrize("kw,status", [
     (dict(V=-1), INVALID), (dict(H=0), INVALID), (dict(K=0), INVALID), (dict(K=65), UNSUPPORTED),
     (dict(gv=None), INVALID), (dict(p2f=None), INVALID), (dict(faces=None), INVALID),
-    (dict(blur=-1.0), INVALID), (dict(blur=float("nan")), INVALID), (dict(flags=2), INVALID),
+    (dict(blur=-1.0), INVALID), (dict(blur=float("nan")), INVALID), (dict(flags=0x10), INVALID), (dict(flags=0x80000000), INVALID),
     (dict(ws=None, flags=1), WS_SMALL), (dict(ws_bytes=100, flags=1), WS_SMALL),
 ])
 def test_backward_rejects_invalid_arguments(dmr, kw, status):
