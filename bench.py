@@ -132,6 +132,40 @@ def blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, steps):
     return out
 
 
+def settings_measurement(dmr, torch, w, verts, faces, offsets, g, outs, gv, ws, dev, steps):
+    """The same step under each rasterizer setting (perspective-correct
+    barycentrics, back-face culling, unclipped barycentrics, all three),
+    timed with events outside the timed step: ms per step and Mpix*K/s."""
+    variants = {"perspective_correct": dmr.DMR_RASTER_PERSPECTIVE_CORRECT,
+                "cull_backfaces": dmr.DMR_RASTER_CULL_BACKFACES,
+                "unclipped_bary": dmr.DMR_RASTER_UNCLIPPED_BARY,
+                "all_three": (dmr.DMR_RASTER_PERSPECTIVE_CORRECT | dmr.DMR_RASTER_CULL_BACKFACES
+                              | dmr.DMR_RASTER_UNCLIPPED_BARY)}
+    stream = torch.cuda.current_stream(dev)
+    out = {}
+    for name, flags in variants.items():
+        def step():
+            dmr.rasterize_meshes_fwd_ex(verts, faces, offsets, w.H, w.W, w.K, w.blur, *outs, ws.buf, flags)
+            dmr.rasterize_meshes_bwd(verts, faces, offsets, w.H, w.W, w.K, w.blur, outs[0], g["zbuf"], g["bary"],
+                                     g["dists"], gv, ws.buf, reuse_forward_workspace=True, settings=flags)
+
+        for _ in range(2):
+            step()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        out[name] = {"ms_per_step": round(ms, 4), "value": round(w.slots / (ms * 1e-3) / 1e6, 1),
+                     "filled_slots": int((outs[0] >= 0).sum().item())}
+    out["unit"] = "Mpix*K/s"
+    return out
+
+
 def cpu_baseline(w, grads_np, seconds: float):
     """The oracle, as it stands, on a bounded sample of the workload's pixels."""
     import numpy as np
@@ -300,6 +334,8 @@ def main():
         "workspace": {k: stats[k] for k in ("required_bytes", "bin_entries", "overflow_bins", "live_faces")},
     }
     line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
+    line["settings"] = settings_measurement(dmr, torch, w, verts, faces, offsets, g, (p2f, zbuf, bary, dists), gv,
+                                            ws, dev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gnp, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -1,6 +1,6 @@
 """Seeded synthetic inputs for the mesh rasterizer.
 
-This package only draws geometry, per-face colours and upstream gradients. It holds none of the
+This package only draws geometry, per-face colours, cameras and upstream gradients. It holds none of the
 rasterizer's arithmetic, so both the CPU oracle (through the tests) and the
 GPU path (through the tests and the benchmark) can consume the same arrays
 without sharing any code of the method itself.
@@ -16,4 +16,7 @@ from .meshes import (  # noqa: F401
     masked_upstream_grads,
     face_colors,
     blend_upstream_grads,
+    vert_offsets,
+    projection_inputs,
+    projection_upstream_grads,
 )

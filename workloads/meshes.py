@@ -314,3 +314,49 @@ def blend_upstream_grads(w: Workload, seed: Optional[int] = None) -> np.ndarray:
     """Dense N(0,1) float32 gradients of the blended RGBA image, [N, H, W, 4]."""
     rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 130363))
     return rng.standard_normal((w.N, w.H, w.W, 4), dtype=np.float32)
+
+
+def vert_offsets(w: Workload) -> np.ndarray:
+    """[N+1] int64 vertex ranges of the meshes: mesh n owns vertices
+    [vo[n], vo[n+1]) (the workloads pack each mesh's vertices together)."""
+    vo = [0]
+    for n in range(w.N):
+        f = w.faces[w.offsets[n]:w.offsets[n + 1]]
+        vo.append(max(vo[-1], int(f.max()) + 1) if f.size else vo[-1])
+    vo[-1] = w.V
+    return np.asarray(vo, np.int64)
+
+
+def projection_inputs(w: Workload, seed: Optional[int] = None):
+    """World-space vertices and per-mesh 4x4 cameras (row-major) whose
+    projection (x/w, y/w, depth) gives back the workload's screen-space
+    vertices up to rounding: each mesh gets a random rotation R, translation
+    t and focal length f in [1.5, 2.5]; its screen vertices (x, y, z) are
+    lifted to view space (x z / f, y z / f, z) and moved to world space by
+    R^T (p - t). The camera is [[f R_0, f t_0], [f R_1, f t_1], [R_2, t_2],
+    [R_2, t_2]].
+
+    Returns (verts_world [V,3] float32, vert_offsets [N+1] int64,
+    cameras [N,4,4] float32)."""
+    rng = np.random.Generator(np.random.PCG64((w.seed if seed is None else seed) + 7919))
+    vo = vert_offsets(w)
+    world = np.zeros((w.V, 3), np.float64)
+    cams = np.zeros((w.N, 4, 4), np.float64)
+    for n in range(w.N):
+        R = _rotation(rng)
+        t = rng.normal(0.0, 1.0, 3)
+        f = rng.uniform(1.5, 2.5)
+        s = w.verts[vo[n]:vo[n + 1]].astype(np.float64)
+        view = np.stack([s[:, 0] * s[:, 2] / f, s[:, 1] * s[:, 2] / f, s[:, 2]], axis=1)
+        world[vo[n]:vo[n + 1]] = (view - t) @ R   # R^T (p - t), row vectors
+        cams[n, 0, :3], cams[n, 0, 3] = f * R[0], f * t[0]
+        cams[n, 1, :3], cams[n, 1, 3] = f * R[1], f * t[1]
+        cams[n, 2, :3], cams[n, 2, 3] = R[2], t[2]
+        cams[n, 3, :3], cams[n, 3, 3] = R[2], t[2]
+    return world.astype(np.float32), vo, cams.astype(np.float32)
+
+
+def projection_upstream_grads(w: Workload, seed: Optional[int] = None) -> np.ndarray:
+    """Dense N(0,1) float32 gradients of the projected vertices, [V, 3]."""
+    rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 15485863))
+    return rng.standard_normal((w.V, 3), dtype=np.float32)
