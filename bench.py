@@ -132,6 +132,49 @@ def blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, steps):
     return out
 
 
+def projection_measurement(dmr, torch, w, dev, steps):
+    """The upstream projection of the workload's meshes (world space to
+    NDC through one camera per mesh), forward and backward with the camera
+    gradient, timed with HIP events outside the timed step, with its HBM
+    roofline: 12 B per vertex read and 12 B written (forward); 24 B read and
+    12 B written (backward), plus the cameras."""
+    from workloads import projection_inputs, projection_upstream_grads
+
+    X, vo, M = projection_inputs(w)
+    Xd = torch.from_numpy(X).to(dev)
+    vod = torch.from_numpy(vo).to(dev)
+    Md = torch.from_numpy(M).to(dev)
+    gd = torch.from_numpy(projection_upstream_grads(w)).to(dev)
+    out = torch.empty_like(Xd)
+    gv = torch.empty_like(Xd)
+    gc = torch.empty_like(Md)
+
+    def run():
+        dmr.dmr_project_fwd(Xd, vod, Md, out)
+        dmr.dmr_project_bwd(Xd, vod, Md, gd, gv, gc)
+
+    for _ in range(2):
+        run()
+    torch.cuda.synchronize()
+    dmr.set_kernel_timing_only(["project_fwd", "project_bwd"])
+    dmr.reset_kernel_timing()
+    for _ in range(steps):
+        run()
+    torch.cuda.synchronize()
+    kt = dmr.kernel_timing()
+    dmr.set_kernel_timing(False)
+    cams = 64 * w.N + 8 * (w.N + 1)
+    res = {}
+    for name, nbytes in (("project_fwd", 24 * w.V + cams), ("project_bwd", 36 * w.V + 2 * cams)):
+        ms, n = kt[name]
+        us = ms / n * 1e3
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"avg_us": round(us, 2), "algorithmic_bytes": nbytes, "achieved_GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    res["vertices"] = w.V
+    return res
+
+
 def settings_measurement(dmr, torch, w, verts, faces, offsets, g, outs, gv, ws, dev, steps):
     """The same step under each rasterizer setting (perspective-correct
     barycentrics, back-face culling, unclipped barycentrics, all three),
@@ -334,6 +377,7 @@ def main():
         "workspace": {k: stats[k] for k in ("required_bytes", "bin_entries", "overflow_bins", "live_faces")},
     }
     line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
+    line["projection"] = projection_measurement(dmr, torch, w, dev, args.steps)
     line["settings"] = settings_measurement(dmr, torch, w, verts, faces, offsets, g, (p2f, zbuf, bary, dists), gv,
                                             ws, dev, args.steps)
     if not args.no_cpu_baseline:

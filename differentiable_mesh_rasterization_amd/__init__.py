@@ -9,7 +9,8 @@ libdmr.so is missing, every call raises.
     rasterize_meshes_fwd / rasterize_meshes_bwd   the two C-ABI entry points
     rasterize_meshes_fwd_ex                       the forward with rasterizer settings
     dmr_blend_fwd / dmr_blend_bwd                 the second stage
-    rasterize_meshes                              autograd-aware convenience
+    dmr_project_fwd / dmr_project_bwd             the upstream projection
+    rasterize_meshes, project_meshes              autograd-aware conveniences
 """
 
 from __future__ import annotations
@@ -34,7 +35,7 @@ EXPORTED = [
     "rasterize_meshes_fwd", "rasterize_meshes_fwd_ex", "rasterize_meshes_bwd", "dmr_workspace_min_size", "dmr_workspace_size_hint",
     "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
-    "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd",
+    "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd", "dmr_project_fwd", "dmr_project_bwd",
 ]
 
 
@@ -103,6 +104,10 @@ def lib(path: Optional[str] = None):
     L.dmr_blend_fwd.argtypes = [P, P, P, I64, I32, P, I64, BP, P, P]
     L.dmr_blend_bwd.restype = ctypes.c_int
     L.dmr_blend_bwd.argtypes = [P, P, P, I64, I32, P, I64, BP, P, P, P, P]
+    L.dmr_project_fwd.restype = ctypes.c_int
+    L.dmr_project_fwd.argtypes = [P, I64, P, I64, P, P, P]
+    L.dmr_project_bwd.restype = ctypes.c_int
+    L.dmr_project_bwd.argtypes = [P, I64, P, I64, P, P, P, P, P]
     if path is None:
         _lib = L
     return L
@@ -284,6 +289,43 @@ def dmr_blend_bwd(pix_to_face: torch.Tensor, zbuf: torch.Tensor, dists: torch.Te
         raise DmrError("dmr_blend_bwd", rc)
 
 
+def _project_inputs(verts_world, mesh_vert_offsets, cameras):
+    dev = verts_world.device
+    _check(verts_world, "verts_world", torch.float32, dev)
+    if verts_world.dim() != 2 or verts_world.shape[1] != 3:
+        raise ValueError("verts_world must be [V, 3]")
+    _check(mesh_vert_offsets, "mesh_vert_offsets", torch.int64, dev)
+    N = mesh_vert_offsets.shape[0] - 1
+    _check(cameras, "cameras", torch.float32, dev, (N, 4, 4))
+    return dev, verts_world.shape[0], N
+
+
+def dmr_project_fwd(verts_world: torch.Tensor, mesh_vert_offsets: torch.Tensor, cameras: torch.Tensor,
+                    verts_ndc: torch.Tensor) -> None:
+    """C-ABI projection on preallocated device tensors (include/dmr.h)."""
+    dev, V, N = _project_inputs(verts_world, mesh_vert_offsets, cameras)
+    _check(verts_ndc, "verts_ndc", torch.float32, dev, (V, 3))
+    rc = lib().dmr_project_fwd(_ptr(verts_world), V, _ptr(mesh_vert_offsets), N, _ptr(cameras), _ptr(verts_ndc),
+                               _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("dmr_project_fwd", rc)
+
+
+def dmr_project_bwd(verts_world: torch.Tensor, mesh_vert_offsets: torch.Tensor, cameras: torch.Tensor,
+                    grad_verts_ndc: torch.Tensor, grad_verts_world: torch.Tensor,
+                    grad_cameras: Optional[torch.Tensor] = None) -> None:
+    """C-ABI backward of the projection (grad_cameras optional)."""
+    dev, V, N = _project_inputs(verts_world, mesh_vert_offsets, cameras)
+    _check(grad_verts_ndc, "grad_verts_ndc", torch.float32, dev, (V, 3))
+    _check(grad_verts_world, "grad_verts_world", torch.float32, dev, (V, 3))
+    _check(grad_cameras, "grad_cameras", torch.float32, dev, (N, 4, 4), optional=True)
+    rc = lib().dmr_project_bwd(_ptr(verts_world), V, _ptr(mesh_vert_offsets), N, _ptr(cameras),
+                               _ptr(grad_verts_ndc), _ptr(grad_verts_world), _ptr(grad_cameras),
+                               _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("dmr_project_bwd", rc)
+
+
 # ----------------------------------------------------------------------------
 # convenience: allocation + autograd
 # ----------------------------------------------------------------------------
@@ -371,6 +413,30 @@ def rasterize_meshes(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets
                 | (0 if clip_barycentric_coords else DMR_RASTER_UNCLIPPED_BARY))
     return _RasterizeMeshes.apply(verts, faces, mesh_face_offsets, int(H), int(W), int(faces_per_pixel),
                                   float(blur_radius), settings)
+
+
+class _ProjectMeshes(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, verts_world, mesh_vert_offsets, cameras):
+        out = torch.empty_like(verts_world)
+        dmr_project_fwd(verts_world, mesh_vert_offsets, cameras, out)
+        ctx.save_for_backward(verts_world, mesh_vert_offsets, cameras)
+        return out
+
+    @staticmethod
+    def backward(ctx, g):
+        verts_world, offs, cameras = ctx.saved_tensors
+        gv = torch.empty_like(verts_world)
+        gc = torch.empty_like(cameras) if ctx.needs_input_grad[2] else None
+        dmr_project_bwd(verts_world, offs, cameras, g.contiguous(), gv, gc)
+        return gv, None, gc
+
+
+def project_meshes(verts_world: torch.Tensor, mesh_vert_offsets: torch.Tensor, cameras: torch.Tensor):
+    """Projects a packed batch of meshes (one 4x4 camera per mesh) to the
+    rasterizer's screen space; differentiable with respect to verts_world
+    and cameras."""
+    return _ProjectMeshes.apply(verts_world, mesh_vert_offsets, cameras)
 
 
 # ----------------------------------------------------------------------------

@@ -33,7 +33,7 @@ std::mutex g_timing_mu;
 
 const char* const kKernelNames[kKernelCount] = {
     "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_slots",
-    "blend_fwd", "blend_bwd",
+    "blend_fwd", "blend_bwd", "project_fwd", "project_bwd",
 };
 
 hipEvent_t take_event() {
@@ -262,6 +262,47 @@ dmr_status dmr_blend_bwd(const int64_t* pix_to_face, const float* zbuf, const fl
     a.colors = face_colors; a.F = F; a.prm = *params; a.grad_rgba = grad_rgba; a.grad_zbuf = grad_zbuf;
     a.grad_dists = grad_dists; a.stream = stream;
     return launch_blend_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+namespace {
+
+dmr_status check_project(const float* verts, int64_t V, const int64_t* off, int64_t N, const float* cameras) {
+    if (V < 0 || N < 0) return DMR_ERROR_INVALID_VALUE;
+    if (V > INT64_MAX / 3 || N > INT64_MAX / 16) return DMR_ERROR_UNSUPPORTED;
+    // one 256-vertex workgroup per grid entry
+    if (V > (int64_t)UINT32_MAX * 256) return DMR_ERROR_UNSUPPORTED;
+    // the camera gradient takes 16 workgroups per mesh
+    if (N > (int64_t)(UINT32_MAX / 16)) return DMR_ERROR_UNSUPPORTED;
+    if (V > 0 && (N == 0 || !verts || !off || !cameras)) return DMR_ERROR_INVALID_VALUE;
+    return DMR_SUCCESS;
+}
+
+}  // namespace
+
+dmr_status dmr_project_fwd(const float* verts_world, int64_t V, const int64_t* mesh_vert_offsets, int64_t N,
+                           const float* cameras, float* verts_ndc, hipStream_t stream) {
+    dmr_status st = check_project(verts_world, V, mesh_vert_offsets, N, cameras);
+    if (st != DMR_SUCCESS) return st;
+    if (V == 0) return DMR_SUCCESS;
+    if (!verts_ndc) return DMR_ERROR_INVALID_VALUE;
+    ProjectArgs a{};
+    a.verts = verts_world; a.V = V; a.off = mesh_vert_offsets; a.N = N; a.cameras = cameras; a.out = verts_ndc;
+    a.stream = stream;
+    return launch_project_forward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+dmr_status dmr_project_bwd(const float* verts_world, int64_t V, const int64_t* mesh_vert_offsets, int64_t N,
+                           const float* cameras, const float* grad_verts_ndc, float* grad_verts_world,
+                           float* grad_cameras, hipStream_t stream) {
+    dmr_status st = check_project(verts_world, V, mesh_vert_offsets, N, cameras);
+    if (st != DMR_SUCCESS) return st;
+    if (V > 0 && (!grad_verts_ndc || !grad_verts_world)) return DMR_ERROR_INVALID_VALUE;
+    if (V == 0 && (N == 0 || grad_cameras == nullptr)) return DMR_SUCCESS;
+    ProjectArgs a{};
+    a.verts = verts_world; a.V = V; a.off = mesh_vert_offsets; a.N = N; a.cameras = cameras;
+    a.grad_out = grad_verts_ndc; a.grad_verts = grad_verts_world; a.grad_cameras = grad_cameras;
+    a.stream = stream;
+    return launch_project_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
 }
 
 dmr_status dmr_workspace_stats(const void* workspace, dmr_stats* out, hipStream_t stream) {

@@ -249,6 +249,8 @@ enum KernelId : int32_t {
     kKBackward,
     kKBlendFwd,
     kKBlendBwd,
+    kKProjectFwd,
+    kKProjectBwd,
     kKernelCount
 };
 
@@ -293,12 +295,23 @@ struct BlendArgs {
     hipStream_t stream;
 };
 
+struct ProjectArgs {
+    const float* verts; int64_t V;
+    const int64_t* off; int64_t N;
+    const float* cameras;
+    float* out;                                   // forward
+    const float* grad_out; float* grad_verts; float* grad_cameras;   // backward
+    hipStream_t stream;
+};
+
 // Launch wrappers with optional event timing; return hipSuccess or the error.
 hipError_t launch_binning(const FwdArgs& a, bool sort);
 hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a);
 hipError_t launch_blend_forward(const BlendArgs& a);
 hipError_t launch_blend_backward(const BlendArgs& a);
+hipError_t launch_project_forward(const ProjectArgs& a);
+hipError_t launch_project_backward(const ProjectArgs& a);
 
 // Timing hooks (api.hip).
 void timing_begin(KernelId id, hipStream_t s);

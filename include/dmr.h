@@ -206,6 +206,42 @@ dmr_status dmr_blend_bwd(const int64_t* pix_to_face, const float* zbuf, const fl
                          const float* face_colors, int64_t F, const dmr_blend_params* params,
                          const float* grad_rgba, float* grad_zbuf, float* grad_dists, hipStream_t stream);
 
+/*
+ * Upstream projection: world-space vertices to the screen space the
+ * rasterizer takes, so that gradients reach 3D parameters (rocketrecap
+ * summary, "3:52 Differentiable Renderer": gradients flow from image pixels
+ * back to the 3D model parameters; "22:00 2D-to-3D Reconstruction": several
+ * viewpoints per object). The pages give no camera model; the library's
+ * reading: mesh n is seen through one 4x4 matrix M_n, and a vertex X of mesh
+ * n maps to
+ *     h = M_n (X, 1),   (x, y, z) = (h0 / h3, h1 / h3, h2)
+ * (x, y perspective-divided NDC; the third row gives the depth, e.g. the
+ * view depth for a pinhole camera). Binary32; each h_r is the left-to-right
+ * sum M_r0 X + M_r1 Y + M_r2 Z + M_r3, and both divisions are correctly
+ * rounded.
+ *
+ *   verts_world [V,3] float32; mesh_vert_offsets [N+1] int64: mesh n owns
+ *              vertices [off[n], off[n+1]) (off[0] = 0, non-decreasing,
+ *              off[N] = V; other offsets give unspecified, memory-safe
+ *              results); N >= 1 when V > 0.
+ *   cameras    [N,4,4] float32, row-major.
+ *   verts_ndc  [V,3] float32, overwritten; must not alias verts_world.
+ * Errors: negative sizes, missing pointers or N == 0 with V > 0:
+ * DMR_ERROR_INVALID_VALUE; V above 256 * (2^32 - 1) or N above (2^32 - 1) / 16:
+ * DMR_ERROR_UNSUPPORTED. V == 0
+ * launches nothing.
+ */
+dmr_status dmr_project_fwd(const float* verts_world, int64_t V, const int64_t* mesh_vert_offsets, int64_t N,
+                           const float* cameras, float* verts_ndc, hipStream_t stream);
+
+/* Backward of dmr_project_fwd for the same inputs: grad_verts_ndc [V,3] in,
+ * grad_verts_world [V,3] out (overwritten) and, if grad_cameras is not NULL,
+ * grad_cameras [N,4,4] (overwritten; summed over each mesh's vertices with
+ * float32 atomics, so its rounding may differ between runs). */
+dmr_status dmr_project_bwd(const float* verts_world, int64_t V, const int64_t* mesh_vert_offsets, int64_t N,
+                           const float* cameras, const float* grad_verts_ndc, float* grad_verts_world,
+                           float* grad_cameras, hipStream_t stream);
+
 /* Smallest forward workspace (bytes) for these sizes: face records and bin
  * tables, with room for no per-bin face list. 0 on invalid arguments. */
 size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W);

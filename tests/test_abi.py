@@ -175,3 +175,32 @@ def test_blend_rejects_invalid_arguments(dmr, fn, kw, status):
 def test_blend_with_no_pixels_is_a_no_op(dmr):
     assert _blend_call(dmr, "dmr_blend_fwd", P=0) == SUCCESS
     assert _blend_call(dmr, "dmr_blend_bwd", P=0) == SUCCESS
+
+
+def _project_call(dmr, fn, V=10, N=2, verts=0x1000, off=0x1000, cams=0x1000, out=0x1000, gout=0x1000,
+                  gcam=None):
+    lib = dmr.lib()
+    P = ctypes.c_void_p
+    if fn == "dmr_project_fwd":
+        return lib.dmr_project_fwd(P(verts), V, P(off), N, P(cams), P(out), None)
+    return lib.dmr_project_bwd(P(verts), V, P(off), N, P(cams), P(gout), P(out), P(gcam) if gcam else None, None)
+
+
+@pytest.mark.parametrize("fn", ["dmr_project_fwd", "dmr_project_bwd"])
+@pytest.mark.parametrize("kw,status", [
+    (dict(V=-1), INVALID), (dict(N=-1), INVALID), (dict(N=0), INVALID), (dict(verts=0), INVALID),
+    (dict(off=0), INVALID), (dict(cams=0), INVALID), (dict(out=0), INVALID),
+    (dict(V=1 << 62), UNSUPPORTED), (dict(V=(2 ** 32) * 256), UNSUPPORTED),
+])
+def test_project_rejects_invalid_arguments(dmr, fn, kw, status):
+    assert _project_call(dmr, fn, **kw) == status
+
+
+def test_project_backward_needs_its_upstream_gradient(dmr):
+    assert _project_call(dmr, "dmr_project_bwd", gout=0) == INVALID
+
+
+def test_project_with_no_vertices_is_a_no_op(dmr):
+    # no vertex and no camera gradient asked for: nothing to launch
+    assert _project_call(dmr, "dmr_project_fwd", V=0, N=0, verts=0, off=0, cams=0, out=0) == SUCCESS
+    assert _project_call(dmr, "dmr_project_bwd", V=0, N=0, verts=0, off=0, cams=0, out=0, gout=0) == SUCCESS

@@ -6,7 +6,8 @@ vertices), and central finite differences of its backward pass."""
 import numpy as np
 import pytest
 
-from oracle.project import project_backward, project_forward, project_forward_error_bound
+from oracle.project import (project_backward, project_backward_error_bound, project_forward,
+                            project_forward_error_bound)
 from workloads import make_workload, projection_inputs
 
 
@@ -102,3 +103,33 @@ def test_error_bound_holds_for_float32_evaluation():
     h = [a.astype(f) for a in h]
     out32 = np.stack([(h[0] / h[3]).astype(f), (h[1] / h[3]).astype(f), h[2]], axis=1)
     assert (np.abs(out32 - ref) <= bound).all()
+
+
+def test_backward_error_bound_holds_for_float32_evaluation():
+    w = make_workload("small_hetero")
+    X, vo, M = projection_inputs(w)
+    g = np.random.default_rng(4).standard_normal((w.V, 3)).astype(np.float32)
+    f = np.float32
+    mesh = np.repeat(np.arange(len(vo) - 1), np.diff(vo))
+    Mm = M[mesh]
+    h = [((((Mm[:, r, 0] * X[:, 0]) + (Mm[:, r, 1] * X[:, 1])) + (Mm[:, r, 2] * X[:, 2])) + Mm[:, r, 3]).astype(f)
+         for r in range(4)]
+    px, py = h[0] / h[3], h[1] / h[3]
+    gh = [g[:, 0] / h[3], g[:, 1] / h[3], g[:, 2], -((g[:, 0] * px) + (g[:, 1] * py)) / h[3]]
+    gv = np.stack([(((Mm[:, 0, c] * gh[0]) + (Mm[:, 1, c] * gh[1])) + (Mm[:, 2, c] * gh[2])) + (Mm[:, 3, c] * gh[3])
+                   for c in range(3)], axis=1)
+    assert gv.dtype == np.float32
+    rgx, rgm = project_backward(X, vo, M, g)
+    bv, bm = project_backward_error_bound(X, vo, M, g, cam_sum_depth=np.diff(vo) // 256 + 10)
+    assert (np.abs(gv - rgx) <= bv).all()
+    # camera entries summed in float32, 256 terms at a time (numpy's pairwise
+    # sum within each, depth <= 8), the partial sums one after the other
+    Xh = np.concatenate([X, np.ones((len(X), 1), f)], axis=1)
+    gm = np.stack(gh, axis=1)[:, :, None] * Xh[:, None, :]
+    gc = np.zeros(M.shape, f)
+    for n in range(len(vo) - 1):
+        for b0 in range(vo[n], vo[n + 1], 256):
+            gc[n] += gm[b0:min(b0 + 256, vo[n + 1])].sum(0, dtype=f)
+    assert (np.abs(gc - rgm) <= bm + 1e-30).all()
+    # and it is not vacuous: a relative error of 1e-4 on one entry breaks it
+    assert not (np.abs(gv * (1 + 1e-4) - rgx) <= bv).all()
