@@ -360,3 +360,80 @@ def projection_upstream_grads(w: Workload, seed: Optional[int] = None) -> np.nda
     """Dense N(0,1) float32 gradients of the projected vertices, [V, 3]."""
     rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 15485863))
     return rng.standard_normal((w.V, 3), dtype=np.float32)
+
+
+# ----------------------------------------------------------------------------
+# point clouds
+# ----------------------------------------------------------------------------
+
+@dataclasses.dataclass
+class PointWorkload:
+    name: str
+    points: np.ndarray   # [P, 3] float32 (x, y NDC, z depth)
+    offsets: np.ndarray  # [N + 1] int64: cloud n owns points [offsets[n], offsets[n+1])
+    H: int
+    W: int
+    K: int
+    radius: float        # a float32 value, NDC units
+    seed: int
+    grad_seed: int
+
+    @property
+    def N(self) -> int:
+        return int(self.offsets.shape[0] - 1)
+
+    @property
+    def P(self) -> int:
+        return int(self.points.shape[0])
+
+    @property
+    def slots(self) -> int:
+        return self.N * self.H * self.W * self.K
+
+    @property
+    def pixels(self) -> int:
+        return self.N * self.H * self.W
+
+
+def _points_from_meshes(mesh_name, H, W, K, radius):
+    w = make_workload(mesh_name)
+    return w.verts.copy(), vert_offsets(w), H, W, K, radius, w.seed, w.grad_seed
+
+
+def _points_soup(seed):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    clouds = []
+    for n, P in enumerate((5000, 0, 3000)):
+        p = np.empty((P, 3))
+        p[:, 0] = rng.uniform(-1.1, 1.1, P)
+        p[:, 1] = rng.uniform(-1.1, 1.1, P)
+        p[:, 2] = rng.uniform(-0.5, 3.0, P)          # about 1 in 7 behind the camera
+        if P:
+            p[: P // 10] = p[P // 10: 2 * (P // 10)]   # exact duplicates: ties of (z) broken by index
+            g = np.round(p[2 * (P // 10): 3 * (P // 10), :2] * 32) / 32
+            p[2 * (P // 10): 3 * (P // 10), :2] = g  # on a dyadic grid: distances exact
+        clouds.append(p)
+    pts = np.concatenate(clouds).astype(np.float32)
+    offs = np.concatenate([[0], np.cumsum([len(c) for c in clouds])]).astype(np.int64)
+    return pts, offs, 64, 80, 5, 0.03125, seed, seed + 1000
+
+
+# name -> builder; the clouds of the mesh workloads are their vertices
+POINT_CONFIGS = {
+    "points16_256": lambda: _points_from_meshes("hetero16_256", 256, 256, 10, 0.01),
+    "points_small": lambda: _points_from_meshes("small_hetero", 72, 56, 8, 0.03),
+    "points_soup": lambda: _points_soup(3100),
+}
+
+
+def make_point_workload(name: str) -> PointWorkload:
+    pts, offs, H, W, K, radius, seed, grad_seed = POINT_CONFIGS[name]()
+    return PointWorkload(name, pts, offs, H, W, K, float(np.float32(radius)), seed, grad_seed)
+
+
+def point_upstream_grads(w: PointWorkload, seed: Optional[int] = None):
+    """Dense N(0,1) float32 gradients of zbuf and dists, each [N,H,W,K]."""
+    rng = np.random.Generator(np.random.PCG64((w.grad_seed if seed is None else seed) + 32452843))
+    shape = (w.N, w.H, w.W, w.K)
+    return {"zbuf": rng.standard_normal(shape, dtype=np.float32),
+            "dists": rng.standard_normal(shape, dtype=np.float32)}
