@@ -175,6 +175,60 @@ def projection_measurement(dmr, torch, w, dev, steps):
     return res
 
 
+def points_measurement(dmr, torch, dev, steps):
+    """Point-cloud rasterization of the 16 clouds of the same spheres' vertices
+    (225,312 points) at 256x256, K = 10, radius 0.01 NDC: forward + backward
+    per step timed with events, and the fine pass's HBM roofline (16 B per
+    slot written: index, depth, distance; 16 B per live point read)."""
+    from workloads import make_point_workload, point_upstream_grads
+
+    w = make_point_workload("points16_256")
+    pts = torch.from_numpy(w.points).to(dev)
+    off = torch.from_numpy(w.offsets).to(dev)
+    g = {k: torch.from_numpy(v).to(dev) for k, v in point_upstream_grads(w).items()}
+    shape = (w.N, w.H, w.W, w.K)
+    idx = torch.empty(shape, dtype=torch.int64, device=dev)
+    zb = torch.empty(shape, dtype=torch.float32, device=dev)
+    ds = torch.empty(shape, dtype=torch.float32, device=dev)
+    gp = torch.empty_like(pts)
+    ws = torch.empty(dmr.dmr_points_workspace_size_hint(w.N, w.P, w.H, w.W, w.K, w.radius), dtype=torch.uint8,
+                     device=dev)
+
+    def step():
+        dmr.rasterize_points_fwd(pts, off, w.H, w.W, w.K, w.radius, idx, zb, ds, ws)
+        dmr.rasterize_points_bwd(pts, off, w.H, w.W, w.K, idx, g["zbuf"], g["dists"], gp)
+
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    dmr.set_kernel_timing(True)
+    dmr.reset_kernel_timing()
+    for _ in range(min(steps, 10)):
+        step()
+    torch.cuda.synchronize()
+    kt = dmr.kernel_timing()
+    dmr.set_kernel_timing(False)
+    live = dmr.dmr_workspace_stats(ws)["live_faces"]
+    kernels = {k: round(v[0] / v[1] * 1e3, 2) for k, v in kt.items() if v[1] and k in
+               ("zero_fwd", "point_setup", "bin_scan", "bin_fill", "bin_sort", "point_raster", "point_bwd")}
+    fine_bytes = 16 * w.slots + 16 * live
+    fine_us = kernels.get("point_raster")
+    return {"workload": "points16_256", "points": w.P, "slots": w.slots,
+            "filled_slots": int((idx >= 0).sum().item()), "ms_per_step": round(ms, 4),
+            "value": round(w.slots / (ms * 1e-3) / 1e6, 1), "unit": "Mpix*K/s", "kernels_us": kernels,
+            "point_raster_hbm_frac": None if not fine_us else round(fine_bytes / (fine_us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+                                                                     4)}
+
+
 def settings_measurement(dmr, torch, w, verts, faces, offsets, g, outs, gv, ws, dev, steps):
     """The same step under each rasterizer setting (perspective-correct
     barycentrics, back-face culling, unclipped barycentrics, all three),
@@ -378,6 +432,7 @@ def main():
     }
     line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
     line["projection"] = projection_measurement(dmr, torch, w, dev, args.steps)
+    line["points"] = points_measurement(dmr, torch, dev, args.steps)
     line["settings"] = settings_measurement(dmr, torch, w, verts, faces, offsets, g, (p2f, zbuf, bary, dists), gv,
                                             ws, dev, args.steps)
     if not args.no_cpu_baseline:

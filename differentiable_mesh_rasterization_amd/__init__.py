@@ -10,7 +10,9 @@ libdmr.so is missing, every call raises.
     rasterize_meshes_fwd_ex                       the forward with rasterizer settings
     dmr_blend_fwd / dmr_blend_bwd                 the second stage
     dmr_project_fwd / dmr_project_bwd             the upstream projection
-    rasterize_meshes, project_meshes              autograd-aware conveniences
+    rasterize_points_fwd / rasterize_points_bwd   point clouds
+    rasterize_meshes, project_meshes,
+    rasterize_points                              autograd-aware conveniences
 """
 
 from __future__ import annotations
@@ -36,6 +38,7 @@ EXPORTED = [
     "dmr_workspace_stats", "dmr_status_string", "dmr_kernel_count",
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
     "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd", "dmr_project_fwd", "dmr_project_bwd",
+    "rasterize_points_fwd", "rasterize_points_bwd", "dmr_points_workspace_min_size", "dmr_points_workspace_size_hint",
 ]
 
 
@@ -108,6 +111,14 @@ def lib(path: Optional[str] = None):
     L.dmr_project_fwd.argtypes = [P, I64, P, I64, P, P, P]
     L.dmr_project_bwd.restype = ctypes.c_int
     L.dmr_project_bwd.argtypes = [P, I64, P, I64, P, P, P, P, P]
+    L.rasterize_points_fwd.restype = ctypes.c_int
+    L.rasterize_points_fwd.argtypes = [P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P, P, SZ, P]
+    L.rasterize_points_bwd.restype = ctypes.c_int
+    L.rasterize_points_bwd.argtypes = [P, I64, P, I64, I32, I32, I32, P, P, P, P, P]
+    L.dmr_points_workspace_min_size.restype = SZ
+    L.dmr_points_workspace_min_size.argtypes = [I64, I64, I32, I32]
+    L.dmr_points_workspace_size_hint.restype = SZ
+    L.dmr_points_workspace_size_hint.argtypes = [I64, I64, I32, I32, I32, ctypes.c_float]
     if path is None:
         _lib = L
     return L
@@ -326,6 +337,52 @@ def dmr_project_bwd(verts_world: torch.Tensor, mesh_vert_offsets: torch.Tensor, 
         raise DmrError("dmr_project_bwd", rc)
 
 
+def dmr_points_workspace_min_size(N: int, P: int, H: int, W: int) -> int:
+    return int(lib().dmr_points_workspace_min_size(N, P, H, W))
+
+
+def dmr_points_workspace_size_hint(N: int, P: int, H: int, W: int, K: int, radius: float) -> int:
+    return int(lib().dmr_points_workspace_size_hint(N, P, H, W, K, radius))
+
+
+def rasterize_points_fwd(points: torch.Tensor, cloud_offsets: torch.Tensor, H: int, W: int, K: int, radius: float,
+                         idx: torch.Tensor, zbuf: torch.Tensor, dists: torch.Tensor, workspace: torch.Tensor) -> None:
+    """C-ABI point rasterization on preallocated device tensors (include/dmr.h)."""
+    dev = points.device
+    N = cloud_offsets.shape[0] - 1
+    _check(points, "points", torch.float32, dev)
+    _check(cloud_offsets, "cloud_offsets", torch.int64, dev)
+    shape = (N, H, W, K)
+    _check(idx, "idx", torch.int64, dev, shape)
+    _check(zbuf, "zbuf", torch.float32, dev, shape)
+    _check(dists, "dists", torch.float32, dev, shape)
+    _check(workspace, "workspace", torch.uint8, dev)
+    rc = lib().rasterize_points_fwd(_ptr(points), points.shape[0], _ptr(cloud_offsets), N, H, W, K, float(radius),
+                                    _ptr(idx), _ptr(zbuf), _ptr(dists), _ptr(workspace), workspace.numel(),
+                                    _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("rasterize_points_fwd", rc)
+
+
+def rasterize_points_bwd(points: torch.Tensor, cloud_offsets: torch.Tensor, H: int, W: int, K: int,
+                         idx: torch.Tensor, grad_zbuf: Optional[torch.Tensor], grad_dists: Optional[torch.Tensor],
+                         grad_points: torch.Tensor) -> None:
+    """C-ABI backward of the point rasterization (include/dmr.h)."""
+    dev = points.device
+    N = cloud_offsets.shape[0] - 1
+    shape = (N, H, W, K)
+    _check(points, "points", torch.float32, dev)
+    _check(cloud_offsets, "cloud_offsets", torch.int64, dev)
+    _check(idx, "idx", torch.int64, dev, shape)
+    _check(grad_zbuf, "grad_zbuf", torch.float32, dev, shape, optional=True)
+    _check(grad_dists, "grad_dists", torch.float32, dev, shape, optional=True)
+    _check(grad_points, "grad_points", torch.float32, dev, tuple(points.shape))
+    rc = lib().rasterize_points_bwd(_ptr(points), points.shape[0], _ptr(cloud_offsets), N, H, W, K, _ptr(idx),
+                                    _ptr(grad_zbuf), _ptr(grad_dists), _ptr(grad_points), _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("rasterize_points_bwd", rc)
+
+
 # ----------------------------------------------------------------------------
 # convenience: allocation + autograd
 # ----------------------------------------------------------------------------
@@ -437,6 +494,43 @@ def project_meshes(verts_world: torch.Tensor, mesh_vert_offsets: torch.Tensor, c
     rasterizer's screen space; differentiable with respect to verts_world
     and cameras."""
     return _ProjectMeshes.apply(verts_world, mesh_vert_offsets, cameras)
+
+
+class _RasterizePoints(torch.autograd.Function):
+    @staticmethod
+    def forward(ctx, points, offsets, H, W, K, radius):
+        N = offsets.shape[0] - 1
+        dev = points.device
+        idx = torch.empty((N, H, W, K), dtype=torch.int64, device=dev)
+        zbuf = torch.empty((N, H, W, K), dtype=torch.float32, device=dev)
+        dists = torch.empty((N, H, W, K), dtype=torch.float32, device=dev)
+        ws = torch.empty(dmr_points_workspace_size_hint(N, points.shape[0], H, W, K, radius), dtype=torch.uint8,
+                         device=dev)
+        rasterize_points_fwd(points, offsets, H, W, K, radius, idx, zbuf, dists, ws)
+        ctx.save_for_backward(points, offsets, idx)
+        ctx.dims = (H, W, K)
+        ctx.mark_non_differentiable(idx)
+        return idx, zbuf, dists
+
+    @staticmethod
+    def backward(ctx, g_idx, g_zbuf, g_dists):
+        points, offsets, idx = ctx.saved_tensors
+        H, W, K = ctx.dims
+        grad = torch.empty_like(points)
+
+        def c(g):
+            return None if g is None else g.contiguous()
+
+        rasterize_points_bwd(points, offsets, H, W, K, idx, c(g_zbuf), c(g_dists), grad)
+        return grad, None, None, None, None, None
+
+
+def rasterize_points(points: torch.Tensor, cloud_offsets: torch.Tensor, image_size: Tuple[int, int],
+                     points_per_pixel: int = 1, radius: float = 0.01):
+    """Rasterizes a packed batch of point clouds on the GPU: (idx, zbuf,
+    dists), zbuf and dists differentiable with respect to points."""
+    H, W = image_size
+    return _RasterizePoints.apply(points, cloud_offsets, int(H), int(W), int(points_per_pixel), float(radius))
 
 
 # ----------------------------------------------------------------------------

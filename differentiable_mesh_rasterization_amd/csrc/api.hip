@@ -33,7 +33,7 @@ std::mutex g_timing_mu;
 
 const char* const kKernelNames[kKernelCount] = {
     "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_slots",
-    "blend_fwd", "blend_bwd", "project_fwd", "project_bwd",
+    "blend_fwd", "blend_bwd", "project_fwd", "project_bwd", "point_setup", "point_raster", "point_bwd",
 };
 
 hipEvent_t take_event() {
@@ -176,6 +176,7 @@ dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t*
     FwdArgs a;
     a.verts = verts; a.V = V; a.faces = faces; a.F = F; a.off = mesh_face_offsets; a.N = N;
     a.H = H; a.W = W; a.K = K; a.blur = blur_radius; a.settings = flags;
+    a.points = nullptr; a.radius = 0.0f;
     a.pix_to_face = pix_to_face; a.zbuf = zbuf; a.bary = bary; a.dists = dists;
     a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes;
     a.L = L; a.capacity = cap; a.stream = stream;
@@ -303,6 +304,81 @@ dmr_status dmr_project_bwd(const float* verts_world, int64_t V, const int64_t* m
     a.grad_out = grad_verts_ndc; a.grad_verts = grad_verts_world; a.grad_cameras = grad_cameras;
     a.stream = stream;
     return launch_project_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+size_t dmr_points_workspace_min_size(int64_t N, int64_t P, int32_t H, int32_t W) {
+    if (N < 0 || P < 0 || H < 1 || W < 1 || H > DMR_MAX_IMAGE_SIDE || W > DMR_MAX_IMAGE_SIDE) return 0;
+    return fwd_layout(N, P, H, W, sizeof(PointRec)).min_bytes;
+}
+
+size_t dmr_points_workspace_size_hint(int64_t N, int64_t P, int32_t H, int32_t W, int32_t K, float radius) {
+    (void)K;
+    size_t base = dmr_points_workspace_min_size(N, P, H, W);
+    if (base == 0 || !(radius >= 0.0f) || !isfinite(radius)) return 0;
+    FwdLayout L = fwd_layout(N, P, H, W, sizeof(PointRec));
+    // a point's box is 2 radius wide: the bins of a box one bin wider than that
+    double rpx = (double)radius * 0.5 * (double)(H > W ? H : W);
+    double per_point = (1.0 + (2.0 * rpx + 2.0) / kBin) * (1.0 + (2.0 * rpx + 2.0) / kBin);
+    double entries = 2.0 * per_point * (double)P + 4.0 * (double)L.bins + 1024.0;
+    if (entries > (double)INT32_MAX) entries = (double)INT32_MAX;
+    return align_up(base + (size_t)entries * sizeof(int32_t), 256);
+}
+
+namespace {
+
+dmr_status check_points(const float* points, int64_t P, const int64_t* off, int64_t N, int32_t H, int32_t W,
+                        int32_t K, int64_t* slots_out) {
+    if (P < 0 || N < 0 || H < 1 || W < 1 || K < 1) return DMR_ERROR_INVALID_VALUE;
+    if (H > DMR_MAX_IMAGE_SIDE || W > DMR_MAX_IMAGE_SIDE || K > DMR_MAX_K) return DMR_ERROR_UNSUPPORTED;
+    if (P > (int64_t)INT32_MAX - 1) return DMR_ERROR_UNSUPPORTED;   // point ids are 32-bit inside
+    int64_t pix, slots;
+    if (mul_overflows(N, (int64_t)H * W, &pix) || mul_overflows(pix, K, &slots)) return DMR_ERROR_UNSUPPORTED;
+    if (slots > (int64_t)UINT32_MAX * 256) return DMR_ERROR_UNSUPPORTED;   // one backward thread per slot
+    if (P > 0 && points == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (N > 0 && off == nullptr) return DMR_ERROR_INVALID_VALUE;
+    *slots_out = slots;
+    return DMR_SUCCESS;
+}
+
+}  // namespace
+
+dmr_status rasterize_points_fwd(const float* points, int64_t P, const int64_t* cloud_offsets, int64_t N, int32_t H,
+                                int32_t W, int32_t K, float radius, int64_t* idx, float* zbuf, float* dists,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+    int64_t slots = 0;
+    dmr_status st = check_points(points, P, cloud_offsets, N, H, W, K, &slots);
+    if (st != DMR_SUCCESS) return st;
+    if (!isfinite(radius) || radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
+    if (slots == 0) return DMR_SUCCESS;
+    if (!idx || !zbuf || !dists) return DMR_ERROR_INVALID_VALUE;
+    FwdLayout L = fwd_layout(N, P, H, W, sizeof(PointRec));
+    if (L.bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;
+    if (workspace == nullptr || workspace_bytes < L.min_bytes) return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    int64_t cap = (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t));
+    if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
+    FwdArgs a{};
+    a.verts = nullptr; a.V = 0; a.faces = nullptr; a.F = P; a.off = cloud_offsets; a.N = N;
+    a.H = H; a.W = W; a.K = K; a.blur = 0.0f; a.settings = 0u;
+    a.points = points; a.radius = radius;
+    a.pix_to_face = idx; a.zbuf = zbuf; a.bary = nullptr; a.dists = dists;
+    a.ws = static_cast<char*>(workspace); a.ws_bytes = workspace_bytes;
+    a.L = L; a.capacity = cap; a.stream = stream;
+    return launch_points_forward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
+}
+
+dmr_status rasterize_points_bwd(const float* points, int64_t P, const int64_t* cloud_offsets, int64_t N, int32_t H,
+                                int32_t W, int32_t K, const int64_t* idx, const float* grad_zbuf,
+                                const float* grad_dists, float* grad_points, hipStream_t stream) {
+    int64_t slots = 0;
+    dmr_status st = check_points(points, P, cloud_offsets, N, H, W, K, &slots);
+    if (st != DMR_SUCCESS) return st;
+    if (P > 0 && grad_points == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (slots > 0 && idx == nullptr) return DMR_ERROR_INVALID_VALUE;
+    if (P == 0) return DMR_SUCCESS;
+    PointBwdArgs a{};
+    a.points = points; a.P = P; a.N = N; a.H = H; a.W = W; a.K = K;
+    a.idx = idx; a.gz = grad_zbuf; a.gd = grad_dists; a.grad_points = grad_points; a.stream = stream;
+    return launch_points_backward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
 }
 
 dmr_status dmr_workspace_stats(const void* workspace, dmr_stats* out, hipStream_t stream) {

@@ -60,6 +60,14 @@ struct alignas(16) FaceBin {
 };
 static_assert(sizeof(FaceBin) == 16, "FaceBin layout");
 
+// Per-point record of the point rasterizer (16 bytes): position, depth and
+// global index (-1: never a candidate: z <= 0 or no pixel centre near it).
+struct alignas(16) PointRec {
+    float x, y, z;
+    int32_t idx;
+};
+static_assert(sizeof(PointRec) == 16, "PointRec layout");
+
 // Workspace header (first 256 bytes of the forward workspace).
 struct WsHeader {
     int64_t required_bytes;
@@ -87,14 +95,16 @@ struct FwdLayout {
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W) {
+// F items (faces, or points) of rec_bytes each: FaceRec for meshes,
+// PointRec for point clouds.
+inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W, size_t rec_bytes = sizeof(FaceRec)) {
     FwdLayout L;
     L.nbx = (W + kBin - 1) / kBin;
     L.nby = (H + kBin - 1) / kBin;
     L.bins = N * L.nbx * L.nby;
     size_t o = sizeof(WsHeader);
     L.off_records = o;
-    o = align_up(o + (size_t)F * sizeof(FaceRec), 256);
+    o = align_up(o + (size_t)F * rec_bytes, 256);
     L.off_fbin = o;
     o = align_up(o + (size_t)F * sizeof(FaceBin), 256);
     L.off_count = o;
@@ -251,6 +261,9 @@ enum KernelId : int32_t {
     kKBlendBwd,
     kKProjectFwd,
     kKProjectBwd,
+    kKPointSetup,
+    kKPointRaster,
+    kKPointBwd,
     kKernelCount
 };
 
@@ -261,6 +274,8 @@ struct FwdArgs {
     int32_t H, W, K;
     float blur;
     uint32_t settings;     // DMR_RASTER_* bits
+    const float* points;   // point clouds instead of meshes (F points, off = cloud offsets)
+    float radius;          // point radius (NDC)
     int64_t* pix_to_face; float* zbuf; float* bary; float* dists;
     char* ws; size_t ws_bytes;
     FwdLayout L;
@@ -310,7 +325,21 @@ hipError_t launch_forward(const FwdArgs& a);
 hipError_t launch_backward(const BwdArgs& a);
 hipError_t launch_blend_forward(const BlendArgs& a);
 hipError_t launch_blend_backward(const BlendArgs& a);
+struct PointBwdArgs {
+    const float* points; int64_t P;
+    int64_t N; int32_t H, W, K;
+    const int64_t* idx; const float* gz; const float* gd;
+    float* grad_points;
+    hipStream_t stream;
+};
+
 hipError_t launch_project_forward(const ProjectArgs& a);
+// Point clouds: the setup pass (binning uses the mesh kernels after it),
+// the fine pass and the backward pass.
+hipError_t launch_point_setup(const FwdArgs& a, PointRec* recs, FaceBin* fbin, int32_t* count, int32_t* block_live,
+                              WsHeader* hdr);
+hipError_t launch_points_forward(const FwdArgs& a);
+hipError_t launch_points_backward(const PointBwdArgs& a);
 hipError_t launch_project_backward(const ProjectArgs& a);
 
 // Timing hooks (api.hip).

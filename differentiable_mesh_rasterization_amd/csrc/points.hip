@@ -1,0 +1,367 @@
+// Point-cloud rasterization on gfx950: for every pixel, the K nearest points
+// of its own cloud within a radius, and the backward pass to the point
+// positions. The pages list point clouds among the data the renderer takes,
+// beside meshes (rocketrecap summary, "2:02 Data Structures and I/O"), with
+// the same two-stage, per-pixel K-nearest selection over heterogeneous
+// batches (gptget.net summary, "Methodology"). The reading is stated in
+// include/dmr.h: a point with z > 0 is a candidate for a pixel when its
+// squared 2D distance to the pixel centre, (px - x)^2 + (py - y)^2 in
+// binary32, is below radius^2 (strict); the K smallest (z, index) are kept.
+//
+// The coarse stage is the mesh rasterizer's: a setup pass writes each
+// point's 16-byte record and pixel box (FaceBin) and counts it into the
+// 16x16 bins the box overlaps; the scan, fill and depth sort are shared.
+// The fine pass gives each bin one 256-thread workgroup, one pixel per
+// thread, stages the bin's points in LDS round by round and keeps a sorted
+// register top-K, stopping once the round's depth bound passes every
+// pixel's K-th key.
+#include <algorithm>
+
+#include "dmr_internal.h"
+
+namespace dmr {
+
+constexpr int kPointThreads = 256;
+
+__device__ __forceinline__ int64_t cloud_of(const int64_t* __restrict__ off, int64_t N, int64_t p) {
+    // last n with off[n] <= p, clamped to [0, N - 1]
+    int64_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int64_t mid = (lo + hi + 1) >> 1;
+        if (off[mid] <= p) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// ---------------------------------------------------------------------------
+// setup: per point record, pixel box and bin counts (LDS histogram for the
+// block's home cloud, global atomics otherwise)
+// ---------------------------------------------------------------------------
+constexpr int kPointHistBins = 4096;
+
+__global__ __launch_bounds__(kSetupThreads) void point_setup_count(
+    const float* __restrict__ pts, int64_t P, const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W,
+    float radius, int32_t nbx, int32_t nby, PointRec* __restrict__ recs, FaceBin* __restrict__ fbin,
+    int32_t* __restrict__ bin_count, int32_t* __restrict__ block_live) {
+    __shared__ int32_t hist[kPointHistBins];
+    __shared__ int64_t home_s, home_lo, home_hi;
+    __shared__ int32_t live_s;
+    const int per_img = nbx * nby;
+    const bool use_lds = per_img <= kPointHistBins;
+    const int64_t first = (int64_t)blockIdx.x * kSetupThreads;
+    if (threadIdx.x == 0) {
+        const int64_t h = cloud_of(off, N, first);
+        home_s = h;
+        home_lo = off[h];
+        home_hi = off[h + 1];
+        live_s = 0;
+    }
+    if (use_lds)
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) hist[q] = 0;
+    __syncthreads();
+    const int64_t home = home_s;
+    const int64_t p = first + threadIdx.x;
+    bool live = false;
+    if (p < P) {
+        const bool in_home = home_lo <= p && p < home_hi;
+        const int64_t n = in_home ? home : cloud_of(off, N, p);
+        const bool ok = in_home || (off[n] <= p && p < off[n + 1]);
+        PointRec r;
+        r.x = pts[3 * p];
+        r.y = pts[3 * p + 1];
+        r.z = pts[3 * p + 2];
+        r.idx = -1;
+        FaceBin fb;
+        fb.box_lo = 0x7fff7fff;  // empty box: lo > hi
+        fb.box_hi = 0;
+        fb.mesh = (int32_t)n;
+        fb.zmin_bits = __float_as_uint(r.z);
+        if (ok && r.z > 0.0f) {
+            // conservative pixel box: the point's square of half-side radius,
+            // grown by a margin far above the rounding of the distance test
+            const float mag = fmaxf(1.0f, fmaxf(fabsf(r.x), fabsf(r.y)));
+            const float m = 1e-5f * mag + 1e-5f * radius;
+            const float xl = r.x - radius - m, xh = r.x + radius + m;
+            const float yl = r.y - radius - m, yh = r.y + radius + m;
+            float jl = ceilf(((xl + 1.0f) * (float)W - 1.0f) * 0.5f);
+            float jh = floorf(((xh + 1.0f) * (float)W - 1.0f) * 0.5f);
+            float il = ceilf(((yl + 1.0f) * (float)H - 1.0f) * 0.5f);
+            float ih = floorf(((yh + 1.0f) * (float)H - 1.0f) * 0.5f);
+            jl = fmaxf(jl, 0.0f);
+            il = fmaxf(il, 0.0f);
+            jh = fminf(jh, (float)(W - 1));
+            ih = fminf(ih, (float)(H - 1));
+            if (jl <= jh && il <= ih) {
+                const int j0 = (int)jl, j1 = (int)jh, i0 = (int)il, i1 = (int)ih;
+                r.idx = (int32_t)p;
+                fb.box_lo = j0 | (i0 << 16);
+                fb.box_hi = j1 | (i1 << 16);
+                live = true;
+                const bool local = use_lds && n == home;
+                int32_t* cnt = bin_count + n * per_img;
+                for (int by = i0 / kBin; by <= i1 / kBin; ++by)
+                    for (int bx = j0 / kBin; bx <= j1 / kBin; ++bx) {
+                        if (local) atomicAdd(&hist[by * nbx + bx], 1);
+                        else atomicAdd(&cnt[by * nbx + bx], 1);
+                    }
+            }
+        }
+        recs[p] = r;
+        fbin[p] = fb;
+    }
+    const unsigned long long m = __ballot(live);
+    if ((threadIdx.x & 63) == 0 && m) atomicAdd(&live_s, (int32_t)__popcll(m));
+    __syncthreads();
+    if (threadIdx.x == 0) block_live[blockIdx.x] = live_s;
+    if (use_lds) {
+        int32_t* cnt = bin_count + home * per_img;
+        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) {
+            const int32_t c = hist[q];
+            if (c) atomicAdd(&cnt[q], c);
+        }
+    }
+}
+
+hipError_t launch_point_setup(const FwdArgs& a, PointRec* recs, FaceBin* fbin, int32_t* count, int32_t* block_live,
+                              WsHeader* hdr) {
+    (void)hdr;
+    timing_begin(kKPointSetup, a.stream);
+    point_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
+        a.points, a.F, a.off, a.N, a.H, a.W, a.radius, (int32_t)a.L.nbx, (int32_t)a.L.nby, recs, fbin, count,
+        block_live);
+    timing_end(kKPointSetup, a.stream);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// fine pass
+// ---------------------------------------------------------------------------
+
+// Sorted insertion of key k into key[0..KMAX) (ascending; ~0 marks empty).
+template <int KMAX>
+__device__ __forceinline__ void point_topk_insert(uint64_t (&key)[KMAX], uint64_t k) {
+    bool lt[KMAX];
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q) lt[q] = k < key[q];
+#pragma unroll
+    for (int q = KMAX - 1; q > 0; --q) {
+        const uint64_t from = lt[q - 1] ? key[q - 1] : k;
+        key[q] = lt[q] ? from : key[q];
+    }
+    key[0] = lt[0] ? k : key[0];
+}
+
+// Squared distance of the pixel centre to the point, in the fixed order.
+__device__ __forceinline__ float point_d2(float px, float py, float x, float y) {
+    const float dx = px - x, dy = py - y;
+    return dx * dx + dy * dy;
+}
+
+template <int KMAX>
+__global__ __launch_bounds__(kPointThreads) void point_raster(
+    const PointRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t P, const int64_t* __restrict__ off,
+    const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
+    const WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
+    int64_t capacity, int32_t H, int32_t W, int32_t K, float r2, int32_t nbx, int32_t nby,
+    int64_t* __restrict__ out_idx, float* __restrict__ zbuf, float* __restrict__ dists) {
+    __shared__ PointRec spt[kPointThreads];
+    __shared__ uint64_t colmask[kBin][kPointThreads / 64];
+    __shared__ uint64_t rowmask[kBin][kPointThreads / 64];
+    constexpr int kBufKeys = 1024;
+    __shared__ uint64_t kbuf[kBufKeys];
+    const int t = threadIdx.x;
+    const int lane = t & 63, wave = t >> 6;
+    if ((int64_t)blockIdx.x >= (int64_t)hdr->fine_items) return;
+    const int64_t b = (int64_t)(items[blockIdx.x] >> 3);
+    const int64_t per_img = (int64_t)nbx * nby;
+    const int64_t n = b / per_img;
+    const int rem = (int)(b - n * per_img);
+    const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+    // each wave owns an 8x8 quarter of the bin
+    const int il = (wave >> 1) * (kBin / 2) + (lane >> 3);
+    const int jl = (wave & 1) * (kBin / 2) + (lane & 7);
+    const int i = by * kBin + il, j = bx * kBin + jl;
+    const bool valid = i < H && j < W;
+    const float px = pixel_centre(j, W), py = pixel_centre(i, H);
+
+    uint64_t key[KMAX];
+#pragma unroll
+    for (int q = 0; q < KMAX; ++q) key[q] = ~0ull;
+
+    const int32_t cnt = count[b];
+    const int64_t o = offset[b];
+    const bool list_mode = o + cnt <= capacity;
+    const bool sorted = list_mode && cnt <= kSortMax;
+    const float* lb = round_lb + b * kRoundsPerBin;
+    int64_t f0 = off[n], f1 = off[n + 1];
+    f0 = f0 < 0 ? 0 : f0;
+    f1 = f1 > P ? P : f1;
+    const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
+    bool done = !valid;
+
+    for (int64_t base = 0; base < total; base += kPointThreads) {
+        // every point from this round on has z >= lb[round]
+        if (sorted && !done) {
+            if (lb[base / kPointThreads] > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) done = true;
+        }
+        if (__syncthreads_count(!done) == 0) break;
+        const int64_t q = base + t;
+        bool live = false;
+        int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
+        if (q < total) {
+            const int64_t pid = list_mode ? (int64_t)entries[o + q] : f0 + q;
+            const FaceBin fb = fbin[pid];
+            c0 = max((fb.box_lo & 0xffff) - bx * kBin, 0);
+            c1 = min((fb.box_hi & 0xffff) - bx * kBin, kBin - 1);
+            r0 = max((fb.box_lo >> 16) - by * kBin, 0);
+            r1 = min((fb.box_hi >> 16) - by * kBin, kBin - 1);
+            live = c0 <= c1 && r0 <= r1;
+            if (live) spt[t] = recs[pid];
+        }
+#pragma unroll
+        for (int c = 0; c < kBin; ++c) {
+            const uint64_t mc = __ballot(live && c0 <= c && c <= c1);
+            const uint64_t mr = __ballot(live && r0 <= c && c <= r1);
+            if (lane == 0) {
+                colmask[c][wave] = mc;
+                rowmask[c][wave] = mr;
+            }
+        }
+        __syncthreads();
+        if (!done) {
+#pragma unroll 1
+            for (int w = 0; w < kPointThreads / 64; ++w) {
+                uint64_t m = colmask[jl][w] & rowmask[il][w];
+                while (m) {
+                    const int u = w * 64 + __builtin_ctzll(m);
+                    m &= m - 1;
+                    const PointRec r = spt[u];
+                    if (point_d2(px, py, r.x, r.y) < r2) {
+                        const uint64_t kk = ((uint64_t)__float_as_uint(r.z) << 32) | (uint32_t)r.idx;
+                        if (kk < key[KMAX - 1]) point_topk_insert<KMAX>(key, kk);
+                    }
+                }
+            }
+        }
+        __syncthreads();
+    }
+
+    // output: keys through LDS, bin rows written slot-linearly (consecutive
+    // lanes on consecutive slots of a row's contiguous 16*K run)
+    const int row_slots = kBin * K;
+    const int rows_per_pass = max(1, min(kBin, kBufKeys / row_slots));
+    const int64_t row0 = ((int64_t)n * H + by * kBin) * W + bx * kBin;
+    for (int ra = 0; ra < kBin; ra += rows_per_pass) {
+        const int rb = min(kBin, ra + rows_per_pass);
+        __syncthreads();
+        if (il >= ra && il < rb) {
+            uint64_t* dst = kbuf + ((il - ra) * kBin + jl) * K;
+#pragma unroll
+            for (int q = 0; q < KMAX; ++q)
+                if (q < K) dst[q] = key[q];
+        }
+        __syncthreads();
+        const int npass = (rb - ra) * row_slots;
+        for (int e = t; e < npass; e += kPointThreads) {
+            const int rr = e / row_slots;
+            const int within = e - rr * row_slots;
+            const int jj = within / K;
+            const int gi = by * kBin + ra + rr, gj = bx * kBin + jj;
+            if (gi >= H || gj >= W) continue;
+            const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
+            const uint64_t kk = kbuf[e];
+            if (kk == ~0ull) {
+                out_idx[so] = -1;
+                zbuf[so] = -1.0f;
+                dists[so] = -1.0f;
+            } else {
+                const int32_t pid = (int32_t)(kk & 0xffffffffull);
+                const PointRec r = recs[pid];
+                out_idx[so] = pid;
+                zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
+                dists[so] = point_d2(pixel_centre(gj, W), pixel_centre(gi, H), r.x, r.y);
+            }
+        }
+    }
+}
+
+hipError_t launch_points_forward(const FwdArgs& a) {
+    hipError_t err = launch_binning(a, true);
+    if (err != hipSuccess) return err;
+    char* ws = a.ws;
+    const WsHeader* hdr = reinterpret_cast<const WsHeader*>(ws);
+    const PointRec* recs = reinterpret_cast<const PointRec*>(ws + a.L.off_records);
+    const FaceBin* fbin = reinterpret_cast<const FaceBin*>(ws + a.L.off_fbin);
+    const int32_t* count = reinterpret_cast<const int32_t*>(ws + a.L.off_count);
+    const int64_t* offset = reinterpret_cast<const int64_t*>(ws + a.L.off_offset);
+    const uint32_t* items = reinterpret_cast<const uint32_t*>(ws + a.L.off_items);
+    const float* round_lb = reinterpret_cast<const float*>(ws + a.L.off_roundlb);
+    const int32_t* entries = reinterpret_cast<const int32_t*>(ws + a.L.off_entries);
+    const float r2 = a.radius * a.radius;
+    const dim3 grid((unsigned)a.L.bins);
+    timing_begin(kKPointRaster, a.stream);
+#define DMR_POINTS(KM)                                                                                               \
+    point_raster<KM><<<grid, kPointThreads, 0, a.stream>>>(recs, fbin, a.F, a.off, count, offset, items, hdr,       \
+                                                           entries, round_lb, a.capacity, a.H, a.W, a.K, r2,        \
+                                                           (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face,       \
+                                                           a.zbuf, a.dists)
+    if (a.K <= 1) DMR_POINTS(1);
+    else if (a.K <= 2) DMR_POINTS(2);
+    else if (a.K <= 4) DMR_POINTS(4);
+    else if (a.K <= 8) DMR_POINTS(8);
+    else if (a.K <= 10) DMR_POINTS(10);
+    else if (a.K <= 16) DMR_POINTS(16);
+    else if (a.K <= 32) DMR_POINTS(32);
+    else DMR_POINTS(64);
+#undef DMR_POINTS
+    timing_end(kKPointRaster, a.stream);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// backward: one thread per slot; zbuf = z_q and dists = d2 give
+// dL/dz_q += g_z, dL/dx_q += -2 (px - x_q) g_d, dL/dy_q += -2 (py - y_q) g_d
+// (float atomics: a point reaches only the few pixels within its radius)
+// ---------------------------------------------------------------------------
+__global__ void point_zero(float* p, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t k = i; k < n; k += stride) p[k] = 0.0f;
+}
+
+__global__ __launch_bounds__(kPointThreads) void point_backward(const float* __restrict__ pts, int64_t P,
+                                                                int64_t slots, int32_t H, int32_t W, int32_t K,
+                                                                const int64_t* __restrict__ idx,
+                                                                const float* __restrict__ gz,
+                                                                const float* __restrict__ gd,
+                                                                float* __restrict__ grad) {
+    const int64_t s = (int64_t)blockIdx.x * kPointThreads + threadIdx.x;
+    if (s >= slots) return;
+    const int64_t q = idx[s];
+    if (q < 0 || q >= P) return;
+    if (gz) atomicAdd(&grad[3 * q + 2], gz[s]);
+    if (gd) {
+        const int64_t pix = s / K;
+        const int j = (int)(pix % W);
+        const int i = (int)((pix / W) % H);
+        const float g = gd[s];
+        const float px = pixel_centre(j, W), py = pixel_centre(i, H);
+        atomicAdd(&grad[3 * q + 0], -2.0f * (px - pts[3 * q]) * g);
+        atomicAdd(&grad[3 * q + 1], -2.0f * (py - pts[3 * q + 1]) * g);
+    }
+}
+
+hipError_t launch_points_backward(const PointBwdArgs& a) {
+    timing_begin(kKPointBwd, a.stream);
+    const int64_t n3 = 3 * a.P;
+    if (n3 > 0)
+        point_zero<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_points, n3);
+    const int64_t slots = a.N * (int64_t)a.H * a.W * a.K;
+    if (slots > 0 && a.P > 0 && (a.gz || a.gd))
+        point_backward<<<(unsigned)((slots + kPointThreads - 1) / kPointThreads), kPointThreads, 0, a.stream>>>(
+            a.points, a.P, slots, a.H, a.W, a.K, a.idx, a.gz, a.gd, a.grad_points);
+    timing_end(kKPointBwd, a.stream);
+    return hipGetLastError();
+}
+
+}  // namespace dmr

@@ -892,7 +892,10 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
             reinterpret_cast<int32_t*>(hdr), (int64_t)(sizeof(WsHeader) / 4), count, a.L.bins);
         timing_end(kKZeroFwd, a.stream);
     }
-    if (a.F > 0) {
+    if (a.F > 0 && a.points) {
+        hipError_t err = launch_point_setup(a, reinterpret_cast<PointRec*>(recs), fbin, count, block_live, hdr);
+        if (err != hipSuccess) return err;
+    } else if (a.F > 0) {
         timing_begin(kKFaceSetup, a.stream);
         face_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
             a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, a.settings, (int32_t)a.L.nbx,
@@ -901,8 +904,9 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     }
     timing_begin(kKBinScan, a.stream);
     uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
-    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, items, a.L.bins,
-                                                 a.K <= kSplitMaxK ? 1 : 0, block_live,
+    // heavy bins are split into quarter items for the mesh fine pass only
+    const int split = (a.K <= kSplitMaxK && !a.points) ? 1 : 0;
+    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, items, a.L.bins, split, block_live,
                                                  a.F > 0 ? a.L.setup_blocks : 0, a.capacity, a.L.min_bytes, hdr);
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {

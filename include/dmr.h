@@ -242,6 +242,46 @@ dmr_status dmr_project_bwd(const float* verts_world, int64_t V, const int64_t* m
                            const float* cameras, const float* grad_verts_ndc, float* grad_verts_world,
                            float* grad_cameras, hipStream_t stream);
 
+/*
+ * Point clouds: for every pixel, the K nearest points of its own cloud
+ * within a radius (rocketrecap summary, "2:02 Data Structures and I/O":
+ * point clouds beside meshes; gptget.net summary, "Methodology": per-pixel
+ * selection over heterogeneous batches). The pages give no formula; the
+ * library's reading: a point q with z_q > 0 is a candidate for pixel (i, j)
+ * (centre (x, y) as for meshes) when d2 = (x - x_q)^2 + (y - y_q)^2 <
+ * radius * radius (binary32, that order, strict); each pixel keeps the K
+ * candidates of smallest (z_q, q).
+ *
+ *   points     [P,3] float32 x, y NDC, z depth; cloud_offsets [N+1] int64:
+ *              cloud n owns points [off[n], off[n+1]) (as mesh_face_offsets).
+ *   radius     NDC units; finite and >= 0.
+ *   idx [N,H,W,K] int64 global point index (-1 pads); zbuf [N,H,W,K] float32
+ *              z_q (-1 pads); dists [N,H,W,K] float32 d2 (-1 pads).
+ *   workspace  as for meshes, sized by dmr_points_workspace_size_hint();
+ *              too small a workspace keeps the results exact (slow path).
+ * Errors as for rasterize_meshes_fwd; P above INT32_MAX - 1 or more than
+ * 256 * (2^32 - 1) slots: DMR_ERROR_UNSUPPORTED.
+ */
+dmr_status rasterize_points_fwd(const float* points, int64_t P, const int64_t* cloud_offsets, int64_t N,
+                                int32_t H, int32_t W, int32_t K, float radius,
+                                int64_t* idx, float* zbuf, float* dists,
+                                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Backward of rasterize_points_fwd: grad_points [P,3] (overwritten) from the
+ * gradients of zbuf and dists (each may be NULL), for the idx that pass
+ * returned: dL/dz_q += g_z, dL/d(x_q, y_q) += -2 (x - x_q, y - y_q) g_d per
+ * slot, summed with float32 atomics (rounding may differ between runs). */
+dmr_status rasterize_points_bwd(const float* points, int64_t P, const int64_t* cloud_offsets, int64_t N,
+                                int32_t H, int32_t W, int32_t K, const int64_t* idx,
+                                const float* grad_zbuf, const float* grad_dists, float* grad_points,
+                                hipStream_t stream);
+
+/* Workspace of the point rasterizer: minimum (records and bin tables) and
+ * suggested (with room for the per-bin point lists) sizes; 0 on invalid
+ * arguments. */
+size_t dmr_points_workspace_min_size(int64_t N, int64_t P, int32_t H, int32_t W);
+size_t dmr_points_workspace_size_hint(int64_t N, int64_t P, int32_t H, int32_t W, int32_t K, float radius);
+
 /* Smallest forward workspace (bytes) for these sizes: face records and bin
  * tables, with room for no per-bin face list. 0 on invalid arguments. */
 size_t dmr_workspace_min_size(int64_t N, int64_t F, int32_t H, int32_t W);

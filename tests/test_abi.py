@@ -204,3 +204,38 @@ def test_project_with_no_vertices_is_a_no_op(dmr):
     # no vertex and no camera gradient asked for: nothing to launch
     assert _project_call(dmr, "dmr_project_fwd", V=0, N=0, verts=0, off=0, cams=0, out=0) == SUCCESS
     assert _project_call(dmr, "dmr_project_bwd", V=0, N=0, verts=0, off=0, cams=0, out=0, gout=0) == SUCCESS
+
+
+def _points_fwd(dmr, P=10, N=1, H=8, W=8, K=2, radius=0.1, pts=0x1000, off=0x1000, out=0x1000, ws=0x1000,
+                ws_bytes=1 << 20):
+    V = ctypes.c_void_p
+    return dmr.lib().rasterize_points_fwd(V(pts), P, V(off), N, H, W, K, radius, V(out), V(out), V(out), V(ws),
+                                          ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(P=-1), INVALID), (dict(N=-1), INVALID), (dict(H=0), INVALID), (dict(K=0), INVALID),
+    (dict(K=65), UNSUPPORTED), (dict(radius=-0.1), INVALID), (dict(radius=float("nan")), INVALID),
+    (dict(pts=0), INVALID), (dict(off=0), INVALID), (dict(out=0), INVALID),
+    (dict(P=1 << 31), UNSUPPORTED), (dict(N=1 << 20, H=4096, W=4096, K=64), UNSUPPORTED),
+    (dict(ws=0), WS_SMALL), (dict(ws_bytes=64), WS_SMALL),
+])
+def test_points_forward_rejects_invalid_arguments(dmr, kw, status):
+    assert _points_fwd(dmr, **kw) == status
+
+
+def test_points_backward_rejects_invalid_arguments(dmr):
+    V = ctypes.c_void_p
+    L = dmr.lib()
+    f = V(0x1000)
+    assert L.rasterize_points_bwd(f, 10, f, 1, 8, 8, 2, f, None, None, None, None) == INVALID   # no grad_points
+    assert L.rasterize_points_bwd(f, 10, f, 1, 8, 8, 2, None, None, None, f, None) == INVALID   # no idx
+    assert L.rasterize_points_bwd(f, -1, f, 1, 8, 8, 2, f, None, None, f, None) == INVALID
+    assert L.rasterize_points_bwd(None, 0, None, 0, 8, 8, 2, None, None, None, None, None) == SUCCESS
+
+
+def test_points_workspace_sizes(dmr):
+    assert dmr.dmr_points_workspace_min_size(1, 100, 64, 64) > 0
+    assert dmr.dmr_points_workspace_size_hint(1, 100, 64, 64, 4, 0.01) > dmr.dmr_points_workspace_min_size(1, 100, 64, 64)
+    assert dmr.dmr_points_workspace_size_hint(1, 100, 64, 64, 4, -1.0) == 0
+    assert dmr.dmr_points_workspace_min_size(-1, 100, 64, 64) == 0

@@ -1,0 +1,150 @@
+"""Point-cloud rasterization on the GPU (through the C ABI) against its
+oracle (oracle/points.py, binary32 in the same operation order): idx, zbuf
+and dists must match bit for bit, padding included; grad_points within 1e-5
+relative L2 (float32 atomics reorder the sums)."""
+
+import numpy as np
+import pytest
+import torch
+
+from gpu_util import DEV, require_gpu, say, to_dev
+from oracle.points import rasterize_points, rasterize_points_backward
+from parity import rel_l2
+from workloads import make_point_workload, point_upstream_grads
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dmr():
+    return require_gpu()
+
+
+def _gpu(dmr, pts, off, H, W, K, radius, ws_bytes=None):
+    p, o = to_dev(np.asarray(pts, np.float32)), to_dev(np.asarray(off, np.int64))
+    N = len(off) - 1
+    shape = (N, H, W, K)
+    idx = torch.empty(shape, dtype=torch.int64, device=DEV)
+    zb = torch.empty(shape, dtype=torch.float32, device=DEV)
+    ds = torch.empty(shape, dtype=torch.float32, device=DEV)
+    if ws_bytes is None:
+        ws_bytes = dmr.dmr_points_workspace_size_hint(N, p.shape[0], H, W, K, radius)
+    ws = torch.empty(max(int(ws_bytes), 1), dtype=torch.uint8, device=DEV)
+    dmr.rasterize_points_fwd(p, o, H, W, K, radius, idx, zb, ds, ws)
+    torch.cuda.synchronize()
+    return (idx, zb, ds), (p, o), ws
+
+
+def _exact(got, ref):
+    for g, r in zip(got, ref):
+        np.testing.assert_array_equal(g.cpu().numpy(), r)
+
+
+@pytest.mark.parametrize("name", ["points_small", "points_soup"])
+def test_points_full_image(dmr, name):
+    w = make_point_workload(name)
+    say(f"[gpu] points full image {name} N={w.N} P={w.P} {w.H}x{w.W} K={w.K} r={w.radius}")
+    out, (p, o), ws = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    ref = rasterize_points(w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    _exact(out, ref)
+    assert (ref[0] >= 0).sum() > 1000
+    st = dmr.dmr_workspace_stats(ws)
+    assert st["overflow_bins"] == 0
+    g = point_upstream_grads(w)
+    gp = torch.empty_like(p)
+    dmr.rasterize_points_bwd(p, o, w.H, w.W, w.K, out[0], to_dev(g["zbuf"]), to_dev(g["dists"]), gp)
+    refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, ref[0], g["zbuf"], g["dists"])
+    err = rel_l2(gp.cpu().numpy(), refg)
+    say(f"  backward rel L2 = {err:.2e}")
+    assert np.linalg.norm(refg) > 0 and err <= 1e-5
+
+
+def test_points_full_size_sampled(dmr):
+    w = make_point_workload("points16_256")
+    rng = np.random.default_rng(12)
+    pix = np.unique(rng.integers(0, w.pixels, 4000))
+    say(f"[gpu] points full size points16_256 P={w.P}, {len(pix)} sampled pixels")
+    out, (p, o), ws = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    st = dmr.dmr_workspace_stats(ws)
+    say(f"  stats {st}")
+    assert st["overflow_bins"] == 0
+    ref = rasterize_points(w.points, w.offsets, w.H, w.W, w.K, w.radius, pixels=pix)
+    idx_t = torch.from_numpy(pix).to(DEV)
+    for g, r in zip(out, ref):
+        got = g.reshape(-1, w.K).index_select(0, idx_t).cpu().numpy()
+        np.testing.assert_array_equal(got, r)
+    # whole image: filled slots form a prefix, keys ascend
+    idx, zb = out[0], out[1]
+    filled = idx >= 0
+    assert bool((filled[..., 1:] <= filled[..., :-1]).all())
+    z = torch.where(filled, zb, torch.full_like(zb, float("inf")))
+    assert bool((z[..., 1:] >= z[..., :-1]).all())
+    assert filled.float().mean().item() > 0.05
+    # backward: upstream gradients on the sampled pixels only
+    g = point_upstream_grads(w)
+    shape = (w.N, w.H, w.W, w.K)
+    dense = {}
+    for k in ("zbuf", "dists"):
+        full = torch.zeros(shape, dtype=torch.float32, device=DEV)
+        full.view(-1, w.K).index_copy_(0, idx_t, to_dev(g[k].reshape(-1, w.K)[pix]))
+        dense[k] = full
+    gp = torch.empty_like(p)
+    dmr.rasterize_points_bwd(p, o, w.H, w.W, w.K, idx, dense["zbuf"], dense["dists"], gp)
+    refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, ref[0], g["zbuf"].reshape(-1, w.K)[pix],
+                                     g["dists"].reshape(-1, w.K)[pix], pixels=pix)
+    assert rel_l2(gp.cpu().numpy(), refg) <= 1e-5
+
+
+def test_points_small_workspace_is_exact(dmr):
+    w = make_point_workload("points_soup")
+    say("[gpu] points with a minimal workspace (every bin list overflows)")
+    ws_min = dmr.dmr_points_workspace_min_size(w.N, w.P, w.H, w.W)
+    out, _, ws = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius, ws_bytes=ws_min)
+    assert dmr.dmr_workspace_stats(ws)["overflow_bins"] > 0
+    _exact(out, rasterize_points(w.points, w.offsets, w.H, w.W, w.K, w.radius))
+
+
+EDGE_CASES = ["k1", "k64", "radius0", "empty_clouds", "offscreen", "ragged", "dense_bin"]
+
+
+@pytest.mark.parametrize("case", EDGE_CASES)
+def test_points_edge_cases(dmr, case):
+    rng = np.random.default_rng(EDGE_CASES.index(case))
+    H, W, K, radius = 37, 29, 4, 0.05
+    pts = np.concatenate([rng.uniform(-1, 1, (600, 2)), rng.uniform(0.5, 2, (600, 1))], 1)
+    off = [0, 300, 600]
+    if case == "k1":
+        K = 1
+    elif case == "k64":
+        K, radius = 64, 0.15
+    elif case == "radius0":
+        radius = 0.0
+    elif case == "empty_clouds":
+        off = [0, 0, 600, 600]
+    elif case == "offscreen":
+        pts[:, :2] *= 3.0
+    elif case == "ragged":
+        H, W = 1, 53
+    elif case == "dense_bin":
+        # 5000 points within one 16x16 bin: a list longer than the sort holds
+        pts = np.concatenate([rng.uniform(-0.95, -0.9, (5000, 2)), rng.uniform(0.5, 2, (5000, 1))], 1)
+        off, H, W, K, radius = [0, 5000], 64, 64, 8, 0.02
+    pts = pts.astype(np.float32)
+    say(f"[gpu] points edge case {case}")
+    out, _, _ = _gpu(dmr, pts, off, H, W, K, radius)
+    ref = rasterize_points(pts, off, H, W, K, radius)
+    _exact(out, ref)
+    if case == "radius0":
+        assert (ref[0] == -1).all()
+
+
+def test_points_autograd(dmr):
+    w = make_point_workload("points_small")
+    p = to_dev(w.points).requires_grad_(True)
+    idx, zb, ds = dmr.rasterize_points(p, to_dev(w.offsets), (w.H, w.W), w.K, w.radius)
+    g = point_upstream_grads(w)
+    ((zb * to_dev(g["zbuf"])).sum() + (ds * to_dev(g["dists"])).sum()).backward()
+    ref = rasterize_points(w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref[0])
+    refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, ref[0], g["zbuf"], g["dists"])
+    assert rel_l2(p.grad.cpu().numpy(), refg) <= 1e-5
