@@ -43,7 +43,7 @@ def algorithmic_bytes(w, filled_slots, live_faces, grads):
 # while these files are unchanged since the counters were taken.
 KERNEL_SOURCES = {
     "fine_raster": ("raster_fwd.hip", "dmr_internal.h"),
-    "backward_slots": ("raster_bwd.hip", "dmr_internal.h"),
+    "backward_slots": ("raster_bwd.hip", "dmr_internal.h", "lds_accum.h"),
 }
 
 

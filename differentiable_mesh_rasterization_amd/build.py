@@ -20,7 +20,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libdmr.so")
 SOURCES = ["api.hip", "raster_fwd.hip", "raster_bwd.hip", "blend.hip", "project.hip", "points.hip"]
-HEADERS = ["dmr_internal.h", os.path.join("..", "..", "include", "dmr.h")]
+HEADERS = ["dmr_internal.h", "lds_accum.h", os.path.join("..", "..", "include", "dmr.h")]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

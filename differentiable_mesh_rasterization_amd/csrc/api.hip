@@ -375,6 +375,7 @@ dmr_status rasterize_points_bwd(const float* points, int64_t P, const int64_t* c
     if (P > 0 && grad_points == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (slots > 0 && idx == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (P == 0) return DMR_SUCCESS;
+    if (fwd_layout(N, P, H, W, sizeof(PointRec)).bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;
     PointBwdArgs a{};
     a.points = points; a.P = P; a.N = N; a.H = H; a.W = W; a.K = K;
     a.idx = idx; a.gz = grad_zbuf; a.gd = grad_dists; a.grad_points = grad_points; a.stream = stream;

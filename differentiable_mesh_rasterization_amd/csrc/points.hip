@@ -18,6 +18,7 @@
 #include <algorithm>
 
 #include "dmr_internal.h"
+#include "lds_accum.h"
 
 namespace dmr {
 
@@ -319,9 +320,12 @@ hipError_t launch_points_forward(const FwdArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: one thread per slot; zbuf = z_q and dists = d2 give
-// dL/dz_q += g_z, dL/dx_q += -2 (px - x_q) g_d, dL/dy_q += -2 (py - y_q) g_d
-// (float atomics: a point reaches only the few pixels within its radius)
+// backward: one workgroup per 16x16 tile, one thread per pixel over its K
+// slots; zbuf = z_q and dists = d2 give dL/dz_q += g_z and
+// dL/d(x_q, y_q) += -2 (px - x_q, py - y_q) g_d. A point reaches the few
+// pixels within its radius, nearly all in one tile: the tile's terms are
+// summed per point in LDS (lds_accum.h), then added to grad_points with one
+// float atomic per (tile, point, coordinate).
 // ---------------------------------------------------------------------------
 __global__ void point_zero(float* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -330,25 +334,36 @@ __global__ void point_zero(float* p, int64_t n) {
 }
 
 __global__ __launch_bounds__(kPointThreads) void point_backward(const float* __restrict__ pts, int64_t P,
-                                                                int64_t slots, int32_t H, int32_t W, int32_t K,
-                                                                const int64_t* __restrict__ idx,
+                                                                int32_t H, int32_t W, int32_t K, int32_t nbx,
+                                                                int32_t nby, const int64_t* __restrict__ idx,
                                                                 const float* __restrict__ gz,
                                                                 const float* __restrict__ gd,
                                                                 float* __restrict__ grad) {
-    const int64_t s = (int64_t)blockIdx.x * kPointThreads + threadIdx.x;
-    if (s >= slots) return;
-    const int64_t q = idx[s];
-    if (q < 0 || q >= P) return;
-    if (gz) atomicAdd(&grad[3 * q + 2], gz[s]);
-    if (gd) {
-        const int64_t pix = s / K;
-        const int j = (int)(pix % W);
-        const int i = (int)((pix / W) % H);
-        const float g = gd[s];
+    __shared__ int32_t hkey[kHashSize];
+    __shared__ unsigned long long hval[kHashSize][3];
+    clear_table(hkey, hval, kPointThreads);
+    __syncthreads();
+    const int64_t per_img = (int64_t)nbx * nby;
+    const int64_t b = blockIdx.x;
+    const int64_t n = b / per_img;
+    const int rem = (int)(b - n * per_img);
+    const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+    const int i = by * kBin + (int)threadIdx.x / kBin, j = bx * kBin + (int)threadIdx.x % kBin;
+    if (i < H && j < W) {
         const float px = pixel_centre(j, W), py = pixel_centre(i, H);
-        atomicAdd(&grad[3 * q + 0], -2.0f * (px - pts[3 * q]) * g);
-        atomicAdd(&grad[3 * q + 1], -2.0f * (py - pts[3 * q + 1]) * g);
+        const int64_t s0 = (((int64_t)n * H + i) * W + j) * K;
+        for (int k = 0; k < K; ++k) {
+            const int64_t q = idx[s0 + k];
+            if (q < 0 || q >= P) continue;
+            const float g_z = gz ? gz[s0 + k] : 0.0f;
+            const float g_d = gd ? gd[s0 + k] : 0.0f;
+            const float gx = -2.0f * (px - pts[3 * q]) * g_d;
+            const float gy = -2.0f * (py - pts[3 * q + 1]) * g_d;
+            vertex_add(hkey, hval, grad, q, gx, gy, g_z, true);
+        }
     }
+    __syncthreads();
+    flush_table(hkey, hval, grad, kPointThreads);
 }
 
 hipError_t launch_points_backward(const PointBwdArgs& a) {
@@ -356,10 +371,11 @@ hipError_t launch_points_backward(const PointBwdArgs& a) {
     const int64_t n3 = 3 * a.P;
     if (n3 > 0)
         point_zero<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_points, n3);
-    const int64_t slots = a.N * (int64_t)a.H * a.W * a.K;
-    if (slots > 0 && a.P > 0 && (a.gz || a.gd))
-        point_backward<<<(unsigned)((slots + kPointThreads - 1) / kPointThreads), kPointThreads, 0, a.stream>>>(
-            a.points, a.P, slots, a.H, a.W, a.K, a.idx, a.gz, a.gd, a.grad_points);
+    const int32_t nbx = (a.W + kBin - 1) / kBin, nby = (a.H + kBin - 1) / kBin;
+    const int64_t bins = a.N * (int64_t)nbx * nby;
+    if (bins > 0 && a.P > 0 && (a.gz || a.gd))
+        point_backward<<<(unsigned)bins, kPointThreads, 0, a.stream>>>(a.points, a.P, a.H, a.W, a.K, nbx, nby,
+                                                                        a.idx, a.gz, a.gd, a.grad_points);
     timing_end(kKPointBwd, a.stream);
     return hipGetLastError();
 }

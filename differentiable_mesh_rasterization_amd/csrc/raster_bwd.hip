@@ -19,6 +19,7 @@
 #include <algorithm>
 
 #include "dmr_internal.h"
+#include "lds_accum.h"
 
 namespace dmr {
 
@@ -145,59 +146,7 @@ __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState&
 }
 
 constexpr int kBwdThreads = kBin * kBin;
-constexpr int kHashBits = 10;
-constexpr int kHashSize = 1 << kHashBits;
-constexpr int kProbe = 32;
 constexpr int kListCap = 1024;   // compacted slots per chunk
-
-// LDS sums are kept in 64-bit fixed point with kFixBits fractional bits: an
-// integer LDS atomic add is about 20x faster than a float one on gfx950 and
-// serialises conflicting lanes without retry loops. A contribution is
-// rounded to a multiple of 2^-kFixBits (3.7e-9); only contributions below
-// kFixLimit in magnitude take this path (larger ones go straight to global
-// float atomics), so a tile's sum for one vertex coordinate -- at most
-// 256 pixels x 64 slots contributions -- stays below 2^34 < 2^(63-kFixBits).
-constexpr int kFixBits = 28;
-constexpr float kFixLimit = 0x1.0p20f;
-
-// (double)v * 2^kFixBits is exact; adding 1.5 * 2^52 rounds it to the
-// nearest integer (ties to even), which then sits in the low mantissa bits
-// of the sum as a two's complement offset from those of 1.5 * 2^52 (valid
-// for magnitudes below 2^51, here below 2^48).
-__device__ __forceinline__ unsigned long long to_fixed(float v) {
-    const double kRound = 6755399441055744.0;   // 1.5 * 2^52
-    const double d = (double)v * (double)(1ull << kFixBits) + kRound;
-    return (unsigned long long)(__double_as_longlong(d) - __double_as_longlong(kRound));
-}
-__device__ __forceinline__ float from_fixed(unsigned long long x) {
-    return (float)((double)(long long)x * (1.0 / (double)(1ull << kFixBits)));
-}
-
-// Adds one vertex's three partials into the tile's LDS hash table, or into
-// grad_verts directly when the table has no room for it or a value is too
-// large for the fixed-point sums.
-__device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*hval)[3],
-                                           float* __restrict__ grad_verts, int64_t vi, float gx, float gy, float gz,
-                                           bool use_hash) {
-    const float lim = kFixLimit;
-    if (use_hash && fabsf(gx) < lim && fabsf(gy) < lim && fabsf(gz) < lim) {
-        const int32_t vid = (int32_t)vi;
-        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - kHashBits);
-        for (int p = 0; p < kProbe; ++p) {
-            const int32_t cur = atomicCAS(&hkey[h], -1, vid);
-            if (cur == -1 || cur == vid) {
-                atomicAdd(&hval[h][0], to_fixed(gx));
-                atomicAdd(&hval[h][1], to_fixed(gy));
-                atomicAdd(&hval[h][2], to_fixed(gz));
-                return;
-            }
-            h = (h + 1) & (kHashSize - 1);
-        }
-    }
-    atomicAdd(&grad_verts[3 * vi + 0], gx);
-    atomicAdd(&grad_verts[3 * vi + 1], gy);
-    atomicAdd(&grad_verts[3 * vi + 2], gz);
-}
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
