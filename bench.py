@@ -308,6 +308,9 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="oracle time budget for cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-timing", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the measurements after the timed step (second stage, projection, point clouds, "
+                         "rasterizer settings)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device copy of BYTES (counter calibration)")
     args = ap.parse_args()
@@ -430,11 +433,12 @@ def main():
         "fwd_bwd_hbm_frac": round((alg["fwd_total"] + alg["bwd_total"]) / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "workspace": {k: stats[k] for k in ("required_bytes", "bin_entries", "overflow_bins", "live_faces")},
     }
-    line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
-    line["projection"] = projection_measurement(dmr, torch, w, dev, args.steps)
-    line["points"] = points_measurement(dmr, torch, dev, args.steps)
-    line["settings"] = settings_measurement(dmr, torch, w, verts, faces, offsets, g, (p2f, zbuf, bary, dists), gv,
-                                            ws, dev, args.steps)
+    if not args.no_extras:
+        line["blend"] = blend_measurement(dmr, torch, w, p2f, zbuf, dists, dev, args.steps)
+        line["projection"] = projection_measurement(dmr, torch, w, dev, args.steps)
+        line["points"] = points_measurement(dmr, torch, dev, args.steps)
+        line["settings"] = settings_measurement(dmr, torch, w, verts, faces, offsets, g, (p2f, zbuf, bary, dists),
+                                                gv, ws, dev, args.steps)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, gnp, args.cpu_seconds)
     print(json.dumps(line), flush=True)
