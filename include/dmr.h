@@ -1,7 +1,15 @@
 /*
  * dmr.h - C ABI of the MI355X (gfx950) K-nearest-face mesh rasterizer.
  *
- * The operation is the face-selection stage of the two-stage rasterizer of
+ * Entry points: the rasterizer's forward and backward passes
+ * (rasterize_meshes_fwd, rasterize_meshes_fwd_ex with settings,
+ * rasterize_meshes_bwd) and their workspace helpers; the second stage that
+ * fuses each pixel's K faces (dmr_blend_fwd / dmr_blend_bwd); point clouds
+ * (rasterize_points_fwd / rasterize_points_bwd); the upstream projection
+ * from world space (dmr_project_fwd / dmr_project_bwd); status strings and
+ * optional per-kernel timing.
+ *
+ * The main operation is the face-selection stage of the two-stage rasterizer of
  * "Accelerating 3D Deep Learning with PyTorch3D": for every pixel, select the
  * faces that influence it and keep the K nearest (gptget.net summary,
  * "Methodology": stage one selects the faces affecting each pixel; nubint.ai
