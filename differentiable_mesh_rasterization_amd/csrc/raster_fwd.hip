@@ -642,7 +642,7 @@ __device__ __forceinline__ void merge_with_lane(uint64_t (&key)[KMAX], int mask)
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
 template <int KMAX, bool PERSP>
-__global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 7 : 1, 8))) void fine_raster(
+__global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 6 : 1, 8))) void fine_raster(
     const FaceRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t F, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
