@@ -78,16 +78,18 @@ def test_blend_full_image(dmr, name, pname):
     _check(ref, rgba.cpu().numpy(), (rz, rd), (gz.cpu().numpy(), gd.cpu().numpy()), sc)
 
 
-def test_blend_full_size_sampled(dmr):
-    w = make_workload("hetero16_256")
+@pytest.mark.parametrize("name,n", [("hetero16_256", 20000), ("soups32_512", 5000)])
+def test_blend_full_size_sampled(dmr, name, n):
+    # soups32_512 has K = 50: four slot chunks per pixel (16, 16, 16, 2)
+    w = make_workload(name)
     prm = PARAMS["sharp"]
-    say("[gpu] blend hetero16_256 sampled")
+    say(f"[gpu] blend {name} sampled")
     g = GpuCase.from_workload(w)
     p2f, zbuf, _, dists = g.forward()
     colors = face_colors(w)
     grad = blend_upstream_grads(w)
     rgba, gz, gd = _blend_gpu(dmr, p2f, zbuf, dists, to_dev(colors), prm, to_dev(grad))
-    pix = sample_pixels(w, 20000)
+    pix = sample_pixels(w, n)
     idx = torch.from_numpy(pix).to(DEV)
     K = w.K
     sel = lambda t, tail: t.reshape((-1,) + tail).index_select(0, idx).cpu().numpy()

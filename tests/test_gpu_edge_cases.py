@@ -2,8 +2,9 @@
 beyond the candidate count, culled and degenerate faces, exact depth ties,
 pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
-thousands of faces in one bin, heavy bins split into quarter items, faces using another mesh's vertices, invalid
-vertex indices, and the hand-worked cases."""
+thousands of faces in one bin, heavy bins split into quarter items, faces
+using another mesh's vertices, the largest image side, hundreds of small
+meshes, invalid vertex indices, and the hand-worked cases."""
 
 import json
 import os
@@ -188,6 +189,28 @@ def faces_use_other_meshes_vertices():
 def large_coordinates():
     v = [[-50, -40, 2], [60, -10, 1], [0, 70, 3], [-0.5, -0.5, 1], [0.5, -0.4, 1], [0.1, 0.6, 1]]
     return v, [[0, 1, 2], [3, 4, 5]], [0, 2], 30, 30, 2, 1e-3
+
+
+@case
+def max_width_image():
+    # the largest image side: 2048 bins per row, faces spread along it
+    rng = np.random.Generator(np.random.PCG64(20))
+    x = rng.uniform(-1.0, 1.0, 60)
+    z = rng.uniform(1.0, 2.0, 60)
+    w = rng.uniform(1e-4, 4e-4, 60)   # 2 to 6 pixels wide
+    v = np.stack([np.stack([x - w, np.full(60, -0.9), z], 1), np.stack([x + w, np.full(60, -0.8), z], 1),
+                  np.stack([x, np.full(60, 0.9), z + 0.1], 1)], 1).reshape(-1, 3).astype(np.float32)
+    return v, np.arange(180).reshape(60, 3), [0, 60], 2, 32767, 3, 1e-9
+
+
+@case
+def many_small_meshes():
+    # 600 meshes of 0-3 faces: setup workgroups span many meshes, so most
+    # bin counts take the global path
+    rng = np.random.Generator(np.random.PCG64(21))
+    sizes = rng.integers(0, 4, 600)
+    v, f = _soup(22, int(sizes.sum()), sigma=0.3)
+    return v, f, np.concatenate([[0], np.cumsum(sizes)]), 8, 8, 2, 1e-2
 
 
 @pytest.mark.parametrize("name", list(CASES))
