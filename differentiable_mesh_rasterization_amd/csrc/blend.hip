@@ -5,10 +5,14 @@
 // keeps: gptget.net summary, "Methodology").
 //
 // Per-slot coverage takes p and 1 - p from one exponential of -|d|/sigma,
-// so that both keep their relative precision when either is close to 0, and
-// the colour weight exponent is formed from the depth difference to the
-// nearest slot, which binary32 holds much more accurately than a difference
-// of normalised inverse depths.
+// so that both keep their relative precision when either is close to 0. The
+// colour weights are summed in the log domain with a running maximum (the
+// largest term is exp(0) = 1): log w_k = log p_k + (zmin - z_k) c with
+// log p_k = -softplus(d_k / sigma), so that a pixel whose weights all
+// underflow binary32 (a sharp sigma far from every face) still gets their
+// ratio, not 0/0. Depths enter as differences to the pixel's first filled
+// slot, which binary32 holds much more accurately than a difference of
+// normalised inverse depths; the common shift cancels in the ratio.
 #include <algorithm>
 
 #include "dmr_internal.h"
@@ -50,19 +54,26 @@ static size_t stage_bytes(int32_t K) { return (size_t)3 * kBlendThreads * stage_
 struct BlendPixel {
     float one_minus_alpha;   // prod (1 - p_k)
     float zmin;              // nearest filled depth
-    float den;               // sum w_k + w_bg
-    float num[3];            // sum w_k c_k + w_bg background
+    float zref;              // depth of the first filled slot (exponent origin)
+    float m;                 // running maximum of the log weights
+    float den;               // sum exp(e_k - m) (+ background)
+    float num[3];            // sum exp(e_k - m) c_k (+ background)
     bool any;
 };
 
 // p = 1 / (1 + exp(d / sigma)) and q = 1 - p: with t = exp(-|d| / sigma),
-// the one that is at least 1/2 is 1 / (1 + t) and the other t / (1 + t).
-__device__ __forceinline__ void coverage(float d, float inv_sigma, float& p, float& q) {
-    const float t = expf(-fabsf(d) * inv_sigma);
+// the one that is at least 1/2 is a = 1 / (1 + t) and the other t a; so
+// log p = log a, or -|d| / sigma + log a. log a lies in [-log 2, 0], where
+// the hardware logarithm's absolute error is a few units of 2^-24.
+__device__ __forceinline__ void coverage(float d, float inv_sigma, float& p, float& q, float& logp) {
+    const float x = d * inv_sigma;
+    const float t = expf(-fabsf(x));
     const float a = 1.0f / (1.0f + t);
     const float b = t * a;
+    const float la = __logf(a);
     p = d <= 0.0f ? a : b;
     q = d <= 0.0f ? b : a;
+    logp = d <= 0.0f ? la : la - x;
 }
 
 // Stage slots [k0, k0 + n) of the block's pixels [pix0, pix0 + np). Element
@@ -101,9 +112,9 @@ __device__ __forceinline__ void stage_chunk(const int64_t* __restrict__ p2f, con
     }
 }
 
-// Accumulates one staged chunk of this lane's pixel into bp. The colour
-// sums are kept relative to the nearest depth seen so far (rescaled when a
-// nearer slot appears).
+// Accumulates one staged chunk of this lane's pixel into bp: the colour sums
+// are kept relative to the largest log weight seen so far (rescaled when a
+// larger one appears).
 __device__ __forceinline__ void accumulate_chunk(const BlendStage& st, const float* __restrict__ colors, int lane,
                                                  int n, float inv_sigma, float inv_range_gamma, BlendPixel& bp) {
     for (int sidx = 0; sidx < n; ++sidx) {
@@ -112,20 +123,23 @@ __device__ __forceinline__ void accumulate_chunk(const BlendStage& st, const flo
         if (f < 0) continue;
         const float z = st.z[e], d = st.d[e];
         const float cr = colors[3 * (int64_t)f + 0], cg = colors[3 * (int64_t)f + 1], cb = colors[3 * (int64_t)f + 2];
-        float p, q;
-        coverage(d, inv_sigma, p, q);
+        float p, q, logp;
+        coverage(d, inv_sigma, p, q, logp);
+        if (!bp.any) bp.zref = z;
         bp.any = true;
         bp.one_minus_alpha *= q;
-        if (z < bp.zmin) {
-            const float r = bp.zmin == __builtin_inff() ? 0.0f : expf((z - bp.zmin) * inv_range_gamma);
+        bp.zmin = fminf(bp.zmin, z);
+        // (zeta_k - zeta_max) / gamma = (zmin - z_k) c, shifted by (zmin - zref) c
+        const float lw = logp + (bp.zref - z) * inv_range_gamma;
+        if (lw > bp.m) {
+            const float r = bp.m == -__builtin_inff() ? 0.0f : expf(bp.m - lw);
             bp.den *= r;
             bp.num[0] *= r;
             bp.num[1] *= r;
             bp.num[2] *= r;
-            bp.zmin = z;
+            bp.m = lw;
         }
-        // zeta_k - zeta_max = (zmin - z_k) / (zfar - znear)
-        const float w = p * expf((bp.zmin - z) * inv_range_gamma);
+        const float w = expf(lw - bp.m);
         bp.den += w;
         bp.num[0] += w * cr;
         bp.num[1] += w * cg;
@@ -134,10 +148,20 @@ __device__ __forceinline__ void accumulate_chunk(const BlendStage& st, const flo
 }
 
 // Adds the background weight w_bg = exp((eps - zeta_max) / gamma), with
-// zeta_max = (zfar - zmin) / (zfar - znear).
-__device__ __forceinline__ void finish_pixel(const dmr_blend_params& prm, BlendPixel& bp) {
+// zeta_max = (zfar - zmin) / (zfar - znear), in the slots' shifted log scale.
+__device__ __forceinline__ void finish_pixel(const dmr_blend_params& prm, float inv_range_gamma, BlendPixel& bp) {
+    if (!bp.any) return;
     const float zeta_max = (prm.zfar - bp.zmin) / (prm.zfar - prm.znear);
-    const float wbg = bp.any ? expf((prm.eps - zeta_max) / prm.gamma) : 0.0f;
+    const float e = (prm.eps - zeta_max) / prm.gamma - (bp.zmin - bp.zref) * inv_range_gamma;
+    if (e > bp.m) {
+        const float r = expf(bp.m - e);
+        bp.den *= r;
+        bp.num[0] *= r;
+        bp.num[1] *= r;
+        bp.num[2] *= r;
+        bp.m = e;
+    }
+    const float wbg = expf(e - bp.m);
     bp.den += wbg;
     bp.num[0] += wbg * prm.background[0];
     bp.num[1] += wbg * prm.background[1];
@@ -152,6 +176,8 @@ __device__ __forceinline__ void blend_block_pixels(const int64_t* __restrict__ p
     const int lane = threadIdx.x;
     bp.one_minus_alpha = 1.0f;
     bp.zmin = __builtin_inff();
+    bp.zref = 0.0f;
+    bp.m = -__builtin_inff();
     bp.den = 0.0f;
     bp.num[0] = bp.num[1] = bp.num[2] = 0.0f;
     bp.any = false;
@@ -163,7 +189,7 @@ __device__ __forceinline__ void blend_block_pixels(const int64_t* __restrict__ p
         __syncthreads();
         if (lane < np) accumulate_chunk(st, colors, lane, n, inv_sigma, inv_range_gamma, bp);
     }
-    finish_pixel(prm, bp);
+    finish_pixel(prm, inv_range_gamma, bp);
 }
 
 __global__ __launch_bounds__(kBlendThreads) void blend_forward(const int64_t* __restrict__ p2f,
@@ -234,13 +260,15 @@ __global__ __launch_bounds__(kBlendThreads) void blend_backward(
                     const float z = st.z[e], d = st.d[e];
                     const float cr = colors[3 * (int64_t)f + 0], cg = colors[3 * (int64_t)f + 1],
                                 cb = colors[3 * (int64_t)f + 2];
-                    float p, q;
-                    coverage(d, inv_sigma, p, q);
-                    const float w = p * expf((bp.zmin - z) * inv_range_gamma);
-                    // d rgb / d w_k = (c_k - rgb) / den, contracted with the rgb gradient
-                    const float gw = ((g.x * (cr - r0) + g.y * (cg - r1)) + g.z * (cb - r2)) * inv_den;
-                    gz = gw * (-w * inv_range_gamma);
-                    gd = gw * (-w * q * inv_sigma) + g.w * (-bp.one_minus_alpha * p * inv_sigma);
+                    float p, q, logp;
+                    coverage(d, inv_sigma, p, q, logp);
+                    // normalised weight w_k / den
+                    const float wn = expf((logp + (bp.zref - z) * inv_range_gamma) - bp.m) * inv_den;
+                    // d rgb / d log w_k = (c_k - rgb) w_k / den, contracted with the rgb
+                    // gradient; d log w_k / dz_k = -c, d log w_k / dd_k = -q_k / sigma
+                    const float gl = ((g.x * (cr - r0) + g.y * (cg - r1)) + g.z * (cb - r2)) * wn;
+                    gz = gl * -inv_range_gamma;
+                    gd = gl * (-q * inv_sigma) + g.w * (-bp.one_minus_alpha * p * inv_sigma);
                 }
                 st.z[e] = gz;
                 st.d[e] = gd;

@@ -50,8 +50,9 @@ def _pixel_terms(p2f, zbuf, dists, colors, prm):
     filled = p2f >= 0
     d = np.where(filled, dists.astype(np.float64), 0.0)
     z = np.where(filled, zbuf.astype(np.float64), 0.0)
-    p = 1.0 / (1.0 + np.exp(d / prm.sigma))
-    q = 1.0 / (1.0 + np.exp(-d / prm.sigma))
+    with np.errstate(over="ignore"):   # exp overflows to inf for a sharp sigma: p or q is then 0
+        p = 1.0 / (1.0 + np.exp(d / prm.sigma))
+        q = 1.0 / (1.0 + np.exp(-d / prm.sigma))
     p = np.where(filled, p, 0.0)
     q = np.where(filled, q, 1.0)
     zeta = (prm.zfar - z) / (prm.zfar - prm.znear)

@@ -60,11 +60,20 @@ def _check(ref_rgba, got_rgba, ref_g=None, got_g=None, scales=None):
             assert np.linalg.norm(err) <= 1e-3 * max(np.linalg.norm(sc), 1e-30)
 
 
-@pytest.mark.parametrize("pname", list(PARAMS))
+# A sigma far below the blur radius: outside faces get coverage weights that
+# underflow binary32 (exp(-d / sigma) with d / sigma up to 333), so a pixel
+# reached only by such faces has every weight, and a far background, below
+# the smallest float. The log-domain sums must still give their ratio.
+VERY_SHARP = BlendParams(sigma=3e-7, gamma=1e-5, znear=1.0, zfar=100.0, eps=1e-10, background=(0.3, 0.6, 0.1))
+
+
+@pytest.mark.parametrize("pname", list(PARAMS) + ["very_sharp"])
 @pytest.mark.parametrize("name", ["sphere64", "spheres8_137", "small_hetero", "small_soups"])
 def test_blend_full_image(dmr, name, pname):
     w = make_workload(name)
-    prm = PARAMS[pname]
+    if pname == "very_sharp" and w.blur > 1e-4:
+        pytest.skip("d / sigma would overflow the binary64 oracle too")
+    prm = VERY_SHARP if pname == "very_sharp" else PARAMS[pname]
     say(f"[gpu] blend {name} {pname}")
     g = GpuCase.from_workload(w)
     p2f, zbuf, _, dists = g.forward()
@@ -75,7 +84,9 @@ def test_blend_full_image(dmr, name, pname):
     ref = blend_forward(hp, hz, hd, colors, prm)
     rz, rd = blend_backward(hp, hz, hd, colors, prm, grad)
     sc = blend_backward_scale(hp, hz, hd, colors, prm, grad)
-    _check(ref, rgba.cpu().numpy(), (rz, rd), (gz.cpu().numpy(), gd.cpu().numpy()), sc)
+    got = rgba.cpu().numpy()
+    assert np.isfinite(got).all() and np.isfinite(ref).all()
+    _check(ref, got, (rz, rd), (gz.cpu().numpy(), gd.cpu().numpy()), sc)
 
 
 @pytest.mark.parametrize("name,n", [("hetero16_256", 20000), ("soups32_512", 5000)])
