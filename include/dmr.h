@@ -226,7 +226,8 @@ dmr_status dmr_blend_bwd(const int64_t* pix_to_face, const float* zbuf, const fl
  * (x, y perspective-divided NDC; the third row gives the depth, e.g. the
  * view depth for a pinhole camera). Binary32; each h_r is the left-to-right
  * sum M_r0 X + M_r1 Y + M_r2 Z + M_r3, and both divisions are correctly
- * rounded.
+ * rounded. A vertex with h3 == 0 (on the camera plane) gets non-finite x, y,
+ * as the definition does.
  *
  *   verts_world [V,3] float32; mesh_vert_offsets [N+1] int64: mesh n owns
  *              vertices [off[n], off[n+1]) (off[0] = 0, non-decreasing,
