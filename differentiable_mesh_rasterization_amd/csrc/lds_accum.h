@@ -35,16 +35,17 @@ __device__ __forceinline__ float from_fixed(unsigned long long x) {
     return (float)((double)(long long)x * (1.0 / (double)(1ull << kFixBits)));
 }
 
-// Adds one id's three partials into the tile's LDS hash table, or into
-// grad_verts directly when the table has no room for it or a value is too
-// large for the fixed-point sums.
+// Adds one id's three partials into the tile's LDS hash table (2^HB
+// entries), or into grad_verts directly when the table has no room for it
+// or a value is too large for the fixed-point sums.
+template <int HB = kHashBits>
 __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*hval)[3],
                                            float* __restrict__ grad_verts, int64_t vi, float gx, float gy, float gz,
                                            bool use_hash) {
     const float lim = kFixLimit;
     if (use_hash && fabsf(gx) < lim && fabsf(gy) < lim && fabsf(gz) < lim) {
         const int32_t vid = (int32_t)vi;
-        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - kHashBits);
+        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - HB);
         for (int p = 0; p < kProbe; ++p) {
             const int32_t cur = atomicCAS(&hkey[h], -1, vid);
             if (cur == -1 || cur == vid) {
@@ -53,7 +54,7 @@ __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*h
                 atomicAdd(&hval[h][2], to_fixed(gz));
                 return;
             }
-            h = (h + 1) & (kHashSize - 1);
+            h = (h + 1) & ((1u << HB) - 1u);
         }
     }
     atomicAdd(&grad_verts[3 * vi + 0], gx);
@@ -63,9 +64,10 @@ __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*h
 
 
 // Flushes a workgroup's table into grad (3 floats per id) with float atomics.
+template <int HB = kHashBits>
 __device__ __forceinline__ void flush_table(const int32_t* hkey, const unsigned long long (*hval)[3],
                                             float* __restrict__ grad, int nthreads) {
-    for (int e = threadIdx.x; e < kHashSize; e += nthreads) {
+    for (int e = threadIdx.x; e < (1 << HB); e += nthreads) {
         const int32_t vid = hkey[e];
         if (vid >= 0) {
             atomicAdd(&grad[3 * (int64_t)vid + 0], from_fixed(hval[e][0]));
@@ -75,8 +77,9 @@ __device__ __forceinline__ void flush_table(const int32_t* hkey, const unsigned 
     }
 }
 
+template <int HB = kHashBits>
 __device__ __forceinline__ void clear_table(int32_t* hkey, unsigned long long (*hval)[3], int nthreads) {
-    for (int e = threadIdx.x; e < kHashSize; e += nthreads) {
+    for (int e = threadIdx.x; e < (1 << HB); e += nthreads) {
         hkey[e] = -1;
         hval[e][0] = 0;
         hval[e][1] = 0;
