@@ -519,20 +519,38 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
 // ---------------------------------------------------------------------------
 // K4: fine rasterization with a register top-K
 // ---------------------------------------------------------------------------
-// Insert k into the ascending list key[0..KMAX-1], dropping the largest.
-// Every slot takes its new value from the old list: slot q keeps key[q] when
-// k is not below it, and otherwise takes k or key[q-1], whichever is larger.
+// Keys of the top-K lists. A list is ordered by (depth, face), i.e. by the
+// 64-bit pattern (depth bits << 32) | face of a depth > 0. Read as a binary64
+// number such a pattern is finite, non-negative and not a NaN, and numeric
+// order is pattern order, so one v_min_f64 or v_max_f64 moves a key; +inf
+// marks an empty slot. The two instructions are written out because the
+// compiler's fmin and fmax first quiet both operands (one more instruction
+// per operand at every step of the chain below).
+constexpr uint64_t kEmptyKeyBits = 0x7ff0000000000000ull;
+
+__device__ __forceinline__ double empty_key() { return __longlong_as_double((long long)kEmptyKeyBits); }
+__device__ __forceinline__ double make_key(float z, int32_t face) {
+    return __hiloint2double((int)__float_as_uint(z), face);
+}
+__device__ __forceinline__ uint64_t key_bits(double k) { return (uint64_t)__double_as_longlong(k); }
+__device__ __forceinline__ double key_min(double a, double b) {
+    double r;
+    asm("v_min_f64 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
+// Push k through the ascending list key[0..KMAX-1]: each slot keeps the
+// smaller of its key and the carried one and carries the larger on, so the
+// list ends as the KMAX smallest of its keys and k.
 template <int KMAX>
-__device__ __forceinline__ void topk_insert(uint64_t (&key)[KMAX], uint64_t k) {
-    bool lt[KMAX];
+__device__ __forceinline__ void topk_push(double (&key)[KMAX], double k) {
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) lt[q] = k < key[q];
-#pragma unroll
-    for (int q = KMAX - 1; q > 0; --q) {
-        const uint64_t from = lt[q - 1] ? key[q - 1] : k;
-        key[q] = lt[q] ? from : key[q];
+    for (int q = 0; q < KMAX; ++q) {
+        double hi;
+        asm("v_max_f64 %0, %1, %2" : "=v"(hi) : "v"(key[q]), "v"(k));
+        asm("v_min_f64 %0, %0, %1" : "+v"(key[q]) : "v"(k));
+        k = hi;
     }
-    key[0] = lt[0] ? k : key[0];
 }
 
 // Squared distance from the pixel to the segment a->b, given dxa = ax - px,
@@ -549,14 +567,13 @@ __device__ __forceinline__ float edge_dist2(float dxa, float dya, float ux, floa
     return rx * rx + ry * ry;
 }
 
-// Candidate test of one (pixel, face) pair against the current last key,
-// with the binary32 operations of the conventions in their fixed order. The
-// depth (and so the key) is formed before the distance: a pair whose key
-// cannot enter the list is dropped without its three edge distances. The
-// result equals testing inclusion first.
+// Key of one (pixel, face) pair, or +inf when the pair is not a candidate
+// or its key is not below `bound`, with the binary32 operations of the
+// conventions in their fixed order. There are no branches: the lanes of a
+// wave evaluate unrelated pairs, and most pairs lie outside their triangle
+// and need the three edge distances anyway.
 template <bool PERSP>
-__device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float py, float blur, uint64_t last,
-                                              uint64_t& kk) {
+__device__ __forceinline__ double pair_key(const FaceRec& r, float px, float py, float blur, double bound) {
     const float dx0 = r.x0 - px, dy0 = r.y0 - py;
     const float dx1 = r.x1 - px, dy1 = r.y1 - py;
     const float dx2 = r.x2 - px, dy2 = r.y2 - py;
@@ -566,7 +583,6 @@ __device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float 
     const float b0 = w0 * r.invA, b1 = w1 * r.invA, b2 = w2 * r.invA;
     const bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
     const bool inside = in_box && (b0 > 0.0f) && (b1 > 0.0f) && (b2 > 0.0f);
-    if (!inside && !(blur > 0.0f)) return false;
     float c0 = b0 < 0.0f ? 0.0f : b0;
     float c1 = b1 < 0.0f ? 0.0f : b1;
     float c2 = b2 < 0.0f ? 0.0f : b2;
@@ -584,65 +600,153 @@ __device__ __forceinline__ bool candidate_key(const FaceRec& r, float px, float 
         const float invS = 1.0f / S;
         z = ((c0 * invS) * r.z0 + (c1 * invS) * r.z1) + (c2 * invS) * r.z2;
     }
-    if (!(z > 0.0f)) return false;
-    kk = ((uint64_t)__float_as_uint(z) << 32) | (uint32_t)r.face;
-    if (!(kk < last)) return false;
-    if (inside) return true;
     const float d0 = edge_dist2(dx0, dy0, r.x1 - r.x0, r.y1 - r.y0, r.il0);
     const float d1 = edge_dist2(dx1, dy1, r.x2 - r.x1, r.y2 - r.y1, r.il1);
     const float d2 = edge_dist2(dx2, dy2, r.x0 - r.x2, r.y0 - r.y2, r.il2);
     float d = d0;
     d = d1 < d ? d1 : d;
     d = d2 < d ? d2 : d;
-    return d < blur;
+    // outside the triangle, d < blur fails for every blur <= 0 (d >= 0)
+    const bool cand = (inside || d < blur) && (z > 0.0f);
+    const double kk = make_key(z, r.face);
+    return (cand && kk < bound) ? kk : empty_key();
+}
+
+// Outputs of a kept (pixel, face) pair: the returned barycentrics and the
+// signed squared distance (negative inside), with the operations of
+// eval_pair in the same order; the distance is edge_dist2's, which equals
+// eval_pair's bit for bit.
+template <bool PERSP>
+__device__ __forceinline__ void slot_outputs(const FaceRec& r, float px, float py, bool unclipped, float& o0,
+                                             float& o1, float& o2, float& sd) {
+    const float dx0 = r.x0 - px, dy0 = r.y0 - py;
+    const float dx1 = r.x1 - px, dy1 = r.y1 - py;
+    const float dx2 = r.x2 - px, dy2 = r.y2 - py;
+    const float w0 = dx1 * dy2 - dy1 * dx2;
+    const float w1 = dx2 * dy0 - dy2 * dx0;
+    const float w2 = dx0 * dy1 - dy0 * dx1;
+    const float b0 = w0 * r.invA, b1 = w1 * r.invA, b2 = w2 * r.invA;
+    const bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    const bool inside = in_box && (b0 > 0.0f) && (b1 > 0.0f) && (b2 > 0.0f);
+    float c0 = b0 < 0.0f ? 0.0f : b0;
+    float c1 = b1 < 0.0f ? 0.0f : b1;
+    float c2 = b2 < 0.0f ? 0.0f : b2;
+    c0 = c0 > 1.0f ? 1.0f : c0;
+    c1 = c1 > 1.0f ? 1.0f : c1;
+    c2 = c2 > 1.0f ? 1.0f : c2;
+    if (PERSP) {
+        float n0, n1, n2;
+        if (unclipped) persp_weights(b0, b1, b2, r.z0, r.z1, r.z2, n0, n1, n2);
+        else persp_weights(c0, c1, c2, r.z0, r.z1, r.z2, n0, n1, n2);
+        const float inv = 1.0f / ((n0 + n1) + n2);
+        o0 = n0 * inv;
+        o1 = n1 * inv;
+        o2 = n2 * inv;
+    } else if (unclipped) {
+        o0 = b0;
+        o1 = b1;
+        o2 = b2;
+    } else {
+        const float invS = 1.0f / ((c0 + c1) + c2);
+        o0 = c0 * invS;
+        o1 = c1 * invS;
+        o2 = c2 * invS;
+    }
+    const float d0 = edge_dist2(dx0, dy0, r.x1 - r.x0, r.y1 - r.y0, r.il0);
+    const float d1 = edge_dist2(dx1, dy1, r.x2 - r.x1, r.y2 - r.y1, r.il1);
+    const float d2 = edge_dist2(dx2, dy2, r.x0 - r.x2, r.y0 - r.y2, r.il2);
+    float d = d0;
+    d = d1 < d ? d1 : d;
+    d = d2 < d ? d2 : d;
+    sd = inside ? -d : d;
 }
 
 // Smallest of the keys held by the four lanes of an aligned lane quad.
-__device__ __forceinline__ uint64_t quad_min(uint64_t x) {
-    uint64_t y = __shfl_xor(x, 1);
-    x = y < x ? y : x;
-    y = __shfl_xor(x, 2);
-    return y < x ? y : x;
+__device__ __forceinline__ double quad_min(double x) {
+    x = key_min(x, __shfl_xor(x, 1));
+    return key_min(x, __shfl_xor(x, 2));
 }
 
 // Merge the sorted lists of the lane `mask` apart into this lane's: both
 // lanes end with the K smallest keys of the two (disjoint) lists.
 template <int KMAX>
-__device__ __forceinline__ void merge_with_lane(uint64_t (&key)[KMAX], int mask) {
-    uint64_t other[KMAX];
+__device__ __forceinline__ void merge_with_lane(double (&key)[KMAX], int mask) {
+    double other[KMAX];
 #pragma unroll
     for (int q = 0; q < KMAX; ++q) other[q] = __shfl_xor(key[q], mask);
 #pragma unroll
     for (int q = 0; q < KMAX; ++q)
-        if (other[q] < key[KMAX - 1]) topk_insert<KMAX>(key, other[q]);
+        if (other[q] < key[KMAX - 1]) topk_push<KMAX>(key, other[q]);
 }
+
+// Exclusive prefix sum over a 256-thread workgroup, and the total.
+__device__ __forceinline__ int block256_exclusive_sum_total(int v, int* wsum, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wsum[wave] = x;
+    __syncthreads();
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kFineThreads / 64; ++w) {
+        const int c = wsum[w];
+        before += (w < wave) ? c : 0;
+        all += c;
+    }
+    __syncthreads();
+    total = all;
+    return before + x - v;
+}
+
+// Pixel centre and current pruning bound of one owner of the fine pass.
+struct OwnerRec {
+    float px, py;
+    double bound;
+};
 
 // Fine pass: one workgroup per work item, in the heaviest-first order of
 // bin_scan (the grid has room for four items per bin; the workgroups past
 // the item count return at once).
 //
-// A whole-bin item gives each thread one pixel of the 16x16 bin; each wave
-// owns an 8x8 quarter, whose pixels' face sets overlap more than those of
-// four full bin rows would. A quarter item gives each of its 64 pixels four
-// lanes (an aligned lane quad, the pixels of a wave forming a 4x4 block);
-// lane s of the quad takes the faces of list positions 64s..64s+63 of every
-// round and keeps its own top-K, the quad shares the smallest of the four
-// K-th keys as its pruning bound (the K-th of any lane bounds the K-th of
-// their union from above), and the four lists are merged at the end.
+// Each thread is an owner: a whole-bin item gives each thread one pixel of
+// the 16x16 bin (each wave owning an 8x8 quarter, whose pixels' face sets
+// overlap more than those of four full bin rows would). A quarter item
+// gives each of its 64 pixels four owners (an aligned lane quad, the pixels
+// of a wave forming a 4x4 block); owner s of the quad takes the faces of
+// list positions 64s..64s+63 of every round and keeps its own top-K, the
+// quad shares the smallest of the four K-th keys as its pruning bound (the
+// K-th of any owner bounds the K-th of their union from above), and the
+// four lists are merged at the end.
 //
 // Each round stages up to 256 of the bin's faces in LDS (one per thread).
 // Every wave then describes the pixel boxes of its 64 faces with ballots:
 // colmask[c] has bit u set when face slot u's box covers bin column c, and
-// rowmask[r] likewise for bin row r. A pixel's candidate faces in the round
-// are colmask[its column] & rowmask[its row], so each lane evaluates only
-// the faces whose box contains its pixel. With a depth-sorted list a pixel
-// stops at the first round whose depth lower bound exceeds its last key, and
-// the workgroup stops the item when all its pixels have.
+// rowmask[r] likewise for bin row r. An owner's candidate faces in the
+// round are colmask[its column] & rowmask[its row].
+//
+// The candidate pairs are evaluated pair-parallel: their number differs
+// from pixel to pixel, so one lane per pixel would leave most lanes of a
+// wave idle. Per window of at most kPairWin pairs, the owners write their
+// pairs' codes (face slot, owner) to positions given by a workgroup prefix
+// sum; all 256 threads evaluate the window's pairs, moving the keys that
+// pass to the front of their owner's positions; and each owner pushes
+// those keys into its register top-K. A pair is tested against its owner's
+// bound from the window's start, which is at least the owner's current
+// one, so a key that passes may still fall off the list: the push drops
+// it. With a depth-sorted list an owner stops at the first round whose
+// depth lower bound exceeds its bound, and the workgroup stops the item
+// when all its owners have.
 // The K output slots of each row of the item's region are then written
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
+constexpr int kPairWin = 1024;
+
 template <int KMAX, bool PERSP>
-__global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 6 : 1, 8))) void fine_raster(
+__global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 4 : 1, 8))) void fine_raster(
     const FaceRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t F, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
@@ -650,16 +754,18 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
     float* __restrict__ dists) {
     __shared__ FaceRec srec[kFineThreads];
-    // the round's masks and depth bounds; the output phase reuses the same
-    // bytes for its list of filled slots
-    __shared__ __align__(16) unsigned char aux[2 * kBin * (kFineThreads / 64) * 8 + kFineThreads * 4];
+    // the round's masks
+    __shared__ __align__(16) unsigned char aux[2 * kBin * (kFineThreads / 64) * 8];
+    __shared__ OwnerRec orec[kFineThreads];
+    __shared__ uint16_t pcode[kPairWin];
+    __shared__ double pres[kPairWin];
+    __shared__ int32_t ofill[kFineThreads];
+    __shared__ float pcx[kBin], pcy[kBin];   // pixel centres of the bin's columns and rows
+    __shared__ int wsum[kFineThreads / 64];
     __shared__ int32_t nfill;
     uint64_t(*colmask)[kFineThreads / 64] = reinterpret_cast<uint64_t(*)[kFineThreads / 64]>(aux);
     uint64_t(*rowmask)[kFineThreads / 64] =
         reinterpret_cast<uint64_t(*)[kFineThreads / 64]>(aux + kBin * (kFineThreads / 64) * 8);
-    float* szlo = reinterpret_cast<float*>(aux + 2 * kBin * (kFineThreads / 64) * 8);
-    uint16_t* olist = reinterpret_cast<uint16_t*>(aux);
-    constexpr int kOutList = (int)(sizeof(aux) / sizeof(uint16_t));
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     const int32_t n_items = hdr->fine_items;
@@ -694,12 +800,12 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         const bool valid = (i < H) && (j < W);
         const float px = pixel_centre(j, W);
         const float py = pixel_centre(i, H);
-        const int w_lo = quarter ? sub : 0;
-        const int w_hi = quarter ? sub + 1 : kFineThreads / 64;
+        if (t < kBin) pcx[t] = pixel_centre(bx * kBin + t, W);
+        else if (t < 2 * kBin) pcy[t - kBin] = pixel_centre(by * kBin + t - kBin, H);
 
-        uint64_t key[KMAX];
+        double key[KMAX];
 #pragma unroll
-        for (int q = 0; q < KMAX; ++q) key[q] = ~0ull;
+        for (int q = 0; q < KMAX; ++q) key[q] = empty_key();
 
         const int32_t cnt = count[b];
         const int64_t o = offset[b];
@@ -711,18 +817,16 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         f1 = f1 > F ? F : f1;
         const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
         bool done = !valid;
-        // pruning bound: this lane's last key, or the quad's smallest
-        uint64_t bound = ~0ull;
 
         for (int64_t base = 0; base < total; base += kFineThreads) {
-            if (quarter) bound = quad_min(key[KMAX - 1]);
-            else bound = key[KMAX - 1];
-            // Every face from this round on has zmin >= lb[round]; a pixel
+            // pruning bound: this owner's last key, or the quad's smallest
+            double bound = quarter ? quad_min(key[KMAX - 1]) : key[KMAX - 1];
+            // Every face from this round on has zmin >= lb[round]; an owner
             // whose bound is below that (with the rounding margin of the
             // depth interpolation) is finished.
             if (sorted && !done) {
                 const float zl = lb[base / kFineThreads] * (1.0f - 0x1.0p-19f) - 1e-30f;
-                if (zl > __uint_as_float((uint32_t)(bound >> 32))) done = true;
+                if (zl > __uint_as_float((uint32_t)(key_bits(bound) >> 32))) done = true;
             }
             if (__syncthreads_count(!done) == 0) break;
             const int64_t q = base + t;
@@ -739,14 +843,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 r0 = max((fb.box_lo >> 16) - by * kBin, reg_r);
                 r1 = min((fb.box_hi >> 16) - by * kBin, reg_r + reg_w - 1);
                 live = (c0 <= c1) && (r0 <= r1);
-                if (live) {
-                    const FaceRec r = recs[fid];
-                    srec[t] = r;
-                    // Depth lower bound: z at any pixel is at least
-                    // min(z0, z1, z2) up to a few roundings, so a face whose
-                    // bound exceeds a pixel's last key cannot enter its list.
-                    szlo[t] = fminf(r.z0, fminf(r.z1, r.z2)) * (1.0f - 0x1.0p-19f) - 1e-30f;
-                }
+                if (live) srec[t] = recs[fid];
             }
 #pragma unroll
             for (int c = 0; c < kBin; ++c) {
@@ -758,19 +855,64 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 }
             }
             __syncthreads();
+            // this owner's candidate faces of the round, one word per wave
+            // of staged faces (a quarter owner reads only its own word)
+            uint64_t m0 = 0, m1 = 0, m2 = 0, m3 = 0;
             if (!done) {
-#pragma unroll 1
-                for (int w = w_lo; w < w_hi; ++w) {
-                    uint64_t m = colmask[jl][w] & rowmask[il][w];
-                    while (m) {
-                        const int u = w * 64 + __builtin_ctzll(m);
-                        m &= m - 1;
-                        const uint64_t last = key[KMAX - 1] < bound ? key[KMAX - 1] : bound;
-                        if (szlo[u] > __uint_as_float((uint32_t)(last >> 32))) continue;
-                        uint64_t kk;
-                        if (candidate_key<PERSP>(srec[u], px, py, blur, last, kk)) topk_insert<KMAX>(key, kk);
-                    }
+                if (quarter) {
+                    m0 = colmask[jl][sub] & rowmask[il][sub];
+                } else {
+                    m0 = colmask[jl][0] & rowmask[il][0];
+                    m1 = colmask[jl][1] & rowmask[il][1];
+                    m2 = colmask[jl][2] & rowmask[il][2];
+                    m3 = colmask[jl][3] & rowmask[il][3];
                 }
+            }
+            int ubase = quarter ? 64 * sub : 0;
+            int left = (int)(__popcll(m0) + __popcll(m1) + __popcll(m2) + __popcll(m3));
+            orec[t] = OwnerRec{px, py, bound};
+            // Windows: every owner with pairs left takes up to cap of them,
+            // cap = kPairWin / (owners with pairs left), so that all of them
+            // progress in every window and the window holds at most kPairWin
+            // pairs. One prefix sum per window gives the positions (low 16
+            // bits) and counts the owners left for the next window (high
+            // bits).
+            int active = __syncthreads_count(left > 0);
+            while (active > 0) {
+                const int cap = kPairWin / active;
+                const int take = left < cap ? left : cap;
+                left -= take;
+                int packed_total;
+                const int start =
+                    block256_exclusive_sum_total(take | ((left > 0) ? 0x10000 : 0), wsum, packed_total) & 0xffff;
+                const int wtotal = packed_total & 0xffff;
+                active = packed_total >> 16;
+                ofill[t] = start;
+                for (int x = 0; x < take; ++x) {
+                    while (m0 == 0) {
+                        m0 = m1;
+                        m1 = m2;
+                        m2 = m3;
+                        m3 = 0;
+                        ubase += 64;
+                    }
+                    const int u = ubase + __builtin_ctzll(m0);
+                    m0 &= m0 - 1;
+                    pcode[start + x] = (uint16_t)(u | (t << 8));
+                }
+                __syncthreads();
+                // the keys that pass go to the front of their owner's range
+                for (int e = t; e < wtotal; e += kFineThreads) {
+                    const uint32_t pc = pcode[e];
+                    const OwnerRec ow = orec[pc >> 8];
+                    const double kk = pair_key<PERSP>(srec[pc & 255u], ow.px, ow.py, blur, ow.bound);
+                    if (key_bits(kk) != kEmptyKeyBits) pres[atomicAdd(&ofill[pc >> 8], 1)] = kk;
+                }
+                __syncthreads();
+                const int passed = ofill[t] - start;
+                for (int x = 0; x < passed; ++x) topk_push<KMAX>(key, pres[start + x]);
+                bound = quarter ? quad_min(key[KMAX - 1]) : key[KMAX - 1];
+                orec[t].bound = bound;
             }
             __syncthreads();
         }
@@ -783,14 +925,21 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         // ---- output: exchange keys through LDS (reusing srec); write each
         // region row's reg_w*K slots with consecutive lanes on consecutive
         // slots (indices, depths and the padding of empty slots), collecting
-        // the filled slots in a list; then evaluate the listed slots densely
-        // for their barycentrics and distances.
+        // the filled slots in a list (reusing the pair buffers); then
+        // evaluate the listed slots densely for their barycentrics and
+        // distances.
         uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
         constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
+        uint16_t* olist = reinterpret_cast<uint16_t*>(pres);
+        constexpr int kOutList = (int)(sizeof(pres) / sizeof(uint16_t));
         const int row_slots = reg_w * K;
         const int rows_per_pass = max(1, min(reg_w, min(kBufKeys, kOutList) / row_slots));
         const bool writer = !quarter || sub == 0;
         const int64_t row0 = ((int64_t)n * H + by * kBin + reg_r) * W + bx * kBin + reg_c;
+        // slot e of a pass -> (row, slot within the row, column): divisions
+        // by multiplication (exact while e * divisor < 2^32)
+        const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
+        const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
         for (int ra = 0; ra < reg_w; ra += rows_per_pass) {
             const int rb = min(reg_w, ra + rows_per_pass);
             const int rr_me = il - reg_r;
@@ -798,7 +947,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 uint64_t* dst = kbuf + ((rr_me - ra) * reg_w + (jl - reg_c)) * K;
 #pragma unroll
                 for (int q = 0; q < KMAX; ++q)
-                    if (q < K) dst[q] = key[q];
+                    if (q < K) dst[q] = key_bits(key[q]);
             }
             if (t == 0) nfill = 0;
             __syncthreads();
@@ -807,13 +956,13 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 const int e = e0 + t;
                 bool filled = false;
                 if (e < npass) {
-                    const int rr = e / row_slots;
+                    const int rr = (int)__umulhi((uint32_t)e, m_row);
                     const int within = e - rr * row_slots;
-                    const int jj = within / K;
+                    const int jj = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
                     if (by * kBin + reg_r + ra + rr < H && bx * kBin + reg_c + jj < W) {
                         const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
                         const uint64_t kk = kbuf[e];
-                        if (kk == ~0ull) {
+                        if (kk == kEmptyKeyBits) {
                             pix_to_face[so] = -1;
                             zbuf[so] = -1.0f;
                             bary[3 * so + 0] = -1.0f;
@@ -840,18 +989,18 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             const int nf = nfill;
             for (int x = t; x < nf; x += kFineThreads) {
                 const int e = olist[x];
-                const int rr = e / row_slots;
+                const int rr = (int)__umulhi((uint32_t)e, m_row);
                 const int within = e - rr * row_slots;
-                const int jj = within / K;
+                const int jj = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
                 const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
                 const int32_t face = (int32_t)(kbuf[e] & 0xffffffffull);
-                PairState st;
-                eval_pair(recs[face], pixel_centre(bx * kBin + reg_c + jj, W),
-                          pixel_centre(by * kBin + reg_r + ra + rr, H), blur, true, settings, st);
-                bary[3 * so + 0] = st.o0;
-                bary[3 * so + 1] = st.o1;
-                bary[3 * so + 2] = st.o2;
-                dists[so] = st.inside ? -st.d2 : st.d2;
+                float o0, o1, o2, sd;
+                slot_outputs<PERSP>(recs[face], pcx[reg_c + jj], pcy[reg_r + ra + rr],
+                                    (settings & DMR_RASTER_UNCLIPPED_BARY) != 0, o0, o1, o2, sd);
+                bary[3 * so + 0] = o0;
+                bary[3 * so + 1] = o1;
+                bary[3 * so + 2] = o2;
+                dists[so] = sd;
             }
             __syncthreads();
         }

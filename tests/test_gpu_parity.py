@@ -95,6 +95,32 @@ def test_forward_full_size_sampled(dmr, name):
     assert st["overflow_bins"] == 0 and st["flags"] == 0
 
 
+def test_forward_full_size_dense_pixels(dmr):
+    """hetero16_256 in the benchmark's launch configuration, compared with the
+    oracle on every pixel of image 0 (a 20,480-face sphere) and on 6,000
+    pixels drawn among those the GPU covers in the four 81,920-face images,
+    where the K lists fill and the depth pruning decides most pairs."""
+    w = make_workload("hetero16_256")
+    g = GpuCase.from_workload(w)
+    out = g.forward()
+    p2f = out[0].cpu().numpy()
+    HW = w.H * w.W
+    sizes = np.diff(w.offsets)
+    big = np.nonzero(sizes == sizes.max())[0]
+    covered = np.concatenate([n * HW + np.nonzero(p2f[n].reshape(HW, w.K)[:, 0] >= 0)[0] for n in big])
+    rng = np.random.Generator(np.random.PCG64(11))
+    pix = np.concatenate([np.arange(HW), np.sort(rng.choice(covered, 6000, replace=False))])
+    say(f"[gpu] forward full size hetero16_256: image 0 whole + 6000 covered pixels of images {list(big)}")
+    got = rows(out, pix, w.K)
+    ref = oracle.rasterize(w.verts, w.faces, w.offsets, w.H, w.W, w.K, w.blur, pixels=pix)
+    rep = compare_forward(ref, got, w.K,
+                          excuse=oracle_excuse(oracle, w.verts, w.faces, w.offsets, w.H, w.W, w.blur, pixel_ids=pix))
+    full_lists = int((ref[0] >= 0).all(axis=1).sum())
+    say(f"  filled={rep['filled_slots']} full lists={full_lists} excused={len(rep['excused'])}")
+    assert full_lists > 4000
+    assert_forward_parity(rep, max_excused_frac=1e-4)
+
+
 @pytest.mark.parametrize("name", list(LARGE))
 def test_backward_full_size_sampled(dmr, name):
     w = make_workload(name)
