@@ -79,7 +79,7 @@ struct WsHeader {
     uint32_t flags;
     uint32_t reserved;
     int32_t fine_items;    // work items of the fine pass (written by the scan)
-    int32_t bwd_next;      // next tile of the backward pass's queue (reset by the backward)
+    int32_t spare;
     int64_t pad[24];
 };
 static_assert(sizeof(WsHeader) == 256, "WsHeader layout");

@@ -46,6 +46,7 @@ __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*h
     if (use_hash && fabsf(gx) < lim && fabsf(gy) < lim && fabsf(gz) < lim) {
         const int32_t vid = (int32_t)vi;
         uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - HB);
+#pragma unroll 1
         for (int p = 0; p < kProbe; ++p) {
             const int32_t cur = atomicCAS(&hkey[h], -1, vid);
             if (cur == -1 || cur == vid) {
@@ -62,6 +63,56 @@ __device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*h
     atomicAdd(&grad_verts[3 * vi + 2], gz);
 }
 
+
+// The three vertices of one face at once: the first probe of all three is
+// issued before any result is waited for, further probes (rare) follow in a
+// loop, then the nine fixed-point adds (or global float atomics for a
+// vertex the table cannot take).
+template <int HB = kHashBits>
+__device__ __forceinline__ void vertex_add3(int32_t* hkey, unsigned long long (*hval)[3],
+                                            float* __restrict__ grad_verts, const int64_t (&vi)[3],
+                                            const float (&g)[9], bool use_hash) {
+    const float lim = kFixLimit;
+    bool elig[3];
+    uint32_t h[3];
+    int32_t cur[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        elig[k] = use_hash && fabsf(g[3 * k]) < lim && fabsf(g[3 * k + 1]) < lim && fabsf(g[3 * k + 2]) < lim;
+        h[k] = ((uint32_t)(int32_t)vi[k] * 2654435761u) >> (32 - HB);
+        cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], -1, (int32_t)vi[k]) : 0;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int32_t vid = (int32_t)vi[k];
+        int slot = -1;
+        if (elig[k]) {
+            if (cur[k] == -1 || cur[k] == vid) {
+                slot = (int)h[k];
+            } else {
+                uint32_t hp = h[k];
+#pragma unroll 1
+                for (int p = 1; p < kProbe; ++p) {
+                    hp = (hp + 1) & ((1u << HB) - 1u);
+                    const int32_t c = atomicCAS(&hkey[hp], -1, vid);
+                    if (c == -1 || c == vid) {
+                        slot = (int)hp;
+                        break;
+                    }
+                }
+            }
+        }
+        if (slot >= 0) {
+            atomicAdd(&hval[slot][0], to_fixed(g[3 * k]));
+            atomicAdd(&hval[slot][1], to_fixed(g[3 * k + 1]));
+            atomicAdd(&hval[slot][2], to_fixed(g[3 * k + 2]));
+        } else {
+            atomicAdd(&grad_verts[3 * vi[k] + 0], g[3 * k]);
+            atomicAdd(&grad_verts[3 * vi[k] + 1], g[3 * k + 1]);
+            atomicAdd(&grad_verts[3 * vi[k] + 2], g[3 * k + 2]);
+        }
+    }
+}
 
 // Flushes a workgroup's table into grad (3 floats per id) with float atomics.
 template <int HB = kHashBits>

@@ -13,7 +13,7 @@
 // hash table, then flushed into grad_verts with one float32 global atomic
 // per (tile, vertex, coordinate).
 //
-// The LDS sums are 64-bit fixed point (see vertex_add): on gfx950 a float
+// The LDS sums are 64-bit fixed point (see to_fixed): on gfx950 a float
 // atomic add in LDS sustains about a third of a lane per clock per CU, an
 // integer one more than seven.
 #include <algorithm>
@@ -23,10 +23,9 @@
 
 namespace dmr {
 
-// Zero fill of grad_verts; also resets the tile queue counter when given.
-__global__ void zero_f32(float* p, int64_t n, int32_t* counter) {
+// Zero fill of grad_verts.
+__global__ void zero_f32(float* p, int64_t n) {
     int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (counter && i == 0) *counter = 0;
     int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (; i < n; i += stride) p[i] = 0.0f;
 }
@@ -146,154 +145,180 @@ __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState&
 }
 
 constexpr int kBwdThreads = kBin * kBin;
-constexpr int kListCap = 1024;   // compacted slots per chunk
+constexpr int kListCap = 1024;   // tile slots read (and at most compacted) per chunk
 
-__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int y = __shfl_up(x, d, 64);
-        if (lane >= d) x += y;
+// One filled slot's inputs, loaded ahead of its evaluation.
+struct SlotIn {
+    FaceRec r;
+    int64_t vi[3];
+    bool ok;
+    float px, py;
+    float gz, gd, gb0, gb1, gb2;
+};
+
+template <uint32_t SETTINGS>
+__device__ __forceinline__ void load_slot(const FaceRec* __restrict__ recs, const float* __restrict__ verts,
+                                          const int64_t* __restrict__ faces, int64_t V, int64_t F, int64_t f,
+                                          int64_t so, float px, float py, const float* __restrict__ gzb,
+                                          const float* __restrict__ gba, const float* __restrict__ gds, SlotIn& in) {
+    in.ok = f >= 0 && f < F;
+    if (!in.ok) return;
+    if (recs) {
+        in.r = recs[f];
+        in.vi[0] = faces[3 * f + 0];
+        in.vi[1] = faces[3 * f + 1];
+        in.vi[2] = faces[3 * f + 2];
+        in.ok = in.r.face >= 0 || (in.vi[0] >= 0 && in.vi[0] < V && in.vi[1] >= 0 && in.vi[1] < V && in.vi[2] >= 0 &&
+                                   in.vi[2] < V);
+    } else {
+        load_face(verts, faces, f, V, in.r, in.vi, in.ok);
     }
-    if (lane == 63) wave_tot[wave] = x;
-    __syncthreads();
-    int base = 0;
-    total = 0;
-#pragma unroll
-    for (int w = 0; w < kBwdThreads / 64; ++w) {
-        const int tw = wave_tot[w];
-        base += (w < wave) ? tw : 0;
-        total += tw;
-    }
-    __syncthreads();
-    return base + x - v;
+    in.px = px;
+    in.py = py;
+    in.gz = gzb ? gzb[so] : 0.0f;
+    in.gd = gds ? gds[so] : 0.0f;
+    in.gb0 = gba ? gba[3 * so + 0] : 0.0f;
+    in.gb1 = gba ? gba[3 * so + 1] : 0.0f;
+    in.gb2 = gba ? gba[3 * so + 2] : 0.0f;
+}
+
+template <uint32_t SETTINGS>
+__device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsigned long long (*hval)[3],
+                                           float* __restrict__ grad_verts, bool use_hash) {
+    if (!in.ok) return;
+    PairState st;
+    eval_pair(in.r, in.px, in.py, __builtin_inff(), true, SETTINGS, st);
+    float g[9];
+    slot_partials(in.r, st, in.px, in.py, in.gz, in.gb0, in.gb1, in.gb2, in.gd, SETTINGS, g);
+    vertex_add3(hkey, hval, grad_verts, in.vi, g, use_hash);
 }
 
 // Tiles come from the grid (one workgroup per tile) or, with the forward's
-// workspace, from a queue in the forward's heaviest-first bin order: each
-// workgroup takes tiles until it meets a bin without faces (those come last
-// and have no filled slot) or the end of the order. SETTINGS holds the
+// workspace, from its heaviest-first bin order, dealt to the resident
+// workgroups in snake order (round r gives workgroup w the tile r*G + w, or
+// r*G + G-1-w for odd r) until a bin without faces (those come last and have
+// no filled slot) or the end of the order. SETTINGS holds the
 // DMR_RASTER_* bits that change the per-slot evaluation (perspective
 // correction, unclipped barycentrics), fixed at compile time so that each
 // variant carries only its own arithmetic.
+//
+// A tile's slots are read slot-linearly in chunks of kListCap (coalesced,
+// all loads of a chunk in flight together); the filled ones are compacted
+// into an LDS list (their order is free: the LDS sums are exact), and each
+// thread evaluates the list's slots two at a time, the second slot's loads
+// issued with the first's.
 template <uint32_t SETTINGS>
 __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const FaceRec* __restrict__ recs, const int32_t* __restrict__ bin_order, const int32_t* __restrict__ bin_count,
-    int32_t* __restrict__ queue, int64_t bins, const float* __restrict__ verts,
-    const int64_t* __restrict__ faces, int64_t V, int64_t F, int32_t H, int32_t W, int32_t K, int32_t nbx,
-    int32_t nby, const int64_t* __restrict__ pix_to_face, const float* __restrict__ gzb,
-    const float* __restrict__ gba, const float* __restrict__ gds, float* __restrict__ grad_verts,
-    int32_t use_hash_arg) {
+    int64_t bins, const float* __restrict__ verts, const int64_t* __restrict__ faces, int64_t V, int64_t F,
+    int32_t H, int32_t W, int32_t K, int32_t nbx, int32_t nby, const int64_t* __restrict__ pix_to_face,
+    const float* __restrict__ gzb, const float* __restrict__ gba, const float* __restrict__ gds,
+    float* __restrict__ grad_verts, int32_t use_hash_arg) {
     __shared__ int32_t hkey[kHashSize];
     __shared__ unsigned long long hval[kHashSize][3];
     __shared__ int32_t lface[kListCap];
-    __shared__ uint16_t lslot[kListCap];   // tile pixel << 8 | slot
-    __shared__ int wave_tot[kBwdThreads / 64];
-    __shared__ int64_t tile_s;
+    __shared__ uint16_t lslot[kListCap];   // slot index within the tile
+    __shared__ int32_t nlist;
     const bool use_hash = use_hash_arg != 0;
     const int64_t per_img = (int64_t)nbx * nby;
-    for (int64_t next = blockIdx.x;; next += gridDim.x) {
-    if (queue) {
-        if (threadIdx.x == 0) {
-            const int32_t q = atomicAdd(queue, 1);
-            int64_t tb = -1;
-            if ((int64_t)q < bins) {
-                tb = bin_order[q];
-                if (bin_count[tb] == 0) tb = -1;
-            }
-            tile_s = tb;
-        }
-        __syncthreads();
-    } else if (threadIdx.x == 0) {
-        tile_s = next < bins ? next : -1;
-    }
-    __syncthreads();
-    const int64_t b = __builtin_amdgcn_readfirstlane((int32_t)tile_s);
-    __syncthreads();   // tile_s is rewritten by the next iteration
-    if (b < 0) break;
-    const int64_t n = b / per_img;
-    const int rem = (int)(b - n * per_img);
-    const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
     const int t = threadIdx.x;
-    const int i = by * kBin + t / kBin;
-    const int j = bx * kBin + (t % kBin);
-    const bool valid = (i < H) && (j < W);
-    for (int e = t; e < kHashSize; e += kBwdThreads) {
-        hkey[e] = -1;
-        hval[e][0] = 0;
-        hval[e][1] = 0;
-        hval[e][2] = 0;
-    }
-    const int64_t pbase = valid ? ((((int64_t)n * H + i) * W + j) * K) : 0;
-    int c = 0;
-    if (valid)
-        for (int k = 0; k < K; ++k) c += pix_to_face[pbase + k] >= 0 ? 1 : 0;
-    int total = 0;
-    const int off = block_exclusive_scan(c, wave_tot, total);
-    for (int chunk = 0; chunk < total; chunk += kListCap) {
-        for (int k = 0; k < c; ++k) {
-            const int e = off + k - chunk;
-            if (e >= 0 && e < kListCap) {
-                lface[e] = (int32_t)pix_to_face[pbase + k];
-                lslot[e] = (uint16_t)((t << 8) | k);
+    const int lane = t & 63;
+    const int64_t G = gridDim.x;
+    // tile slot s -> (row, slot within the row, column): divisions by
+    // multiplication (exact while s * divisor < 2^32)
+    const int row_slots = kBin * K;
+    const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
+    const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
+    const int tile_slots = kBin * row_slots;
+    for (int64_t round = 0;; ++round) {
+        const int64_t idx = round * G + ((round & 1) ? G - 1 - blockIdx.x : blockIdx.x);
+        if (idx >= bins) break;
+        int64_t b = idx;
+        if (bin_order) {
+            b = bin_order[idx];
+            if (bin_count[b] == 0) break;
+        }
+        const int64_t n = b / per_img;
+        const int rem = (int)(b - n * per_img);
+        const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+        const int rows = min(kBin, H - by * kBin), cols = min(kBin, W - bx * kBin);
+        const int64_t tile0 = (((int64_t)n * H + by * kBin) * W + bx * kBin) * K;
+        for (int e = t; e < kHashSize; e += kBwdThreads) {
+            hkey[e] = -1;
+            hval[e][0] = 0;
+            hval[e][1] = 0;
+            hval[e][2] = 0;
+        }
+        for (int cbase = 0; cbase < tile_slots; cbase += kListCap) {
+            if (t == 0) nlist = 0;
+            __syncthreads();
+            int64_t fv[kListCap / kBwdThreads];
+#pragma unroll
+            for (int q = 0; q < kListCap / kBwdThreads; ++q) {
+                const int sidx = cbase + q * kBwdThreads + t;
+                fv[q] = -1;
+                if (sidx < tile_slots) {
+                    const int r = (int)__umulhi((uint32_t)sidx, m_row);
+                    const int within = sidx - r * row_slots;
+                    const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
+                    if (r < rows && col < cols) fv[q] = pix_to_face[tile0 + (int64_t)r * W * K + within];
+                }
+            }
+#pragma unroll
+            for (int q = 0; q < kListCap / kBwdThreads; ++q) {
+                const bool filled = fv[q] >= 0;
+                const uint64_t bal = __ballot(filled);
+                int at = 0;
+                if (lane == 0 && bal) at = atomicAdd(&nlist, (int)__popcll(bal));
+                at = __shfl(at, 0, 64);
+                if (filled) {
+                    const int e = at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                    lface[e] = (int32_t)fv[q];
+                    lslot[e] = (uint16_t)(cbase + q * kBwdThreads + t);
+                }
+            }
+            __syncthreads();
+            const int m = nlist;
+            for (int e = t; e < m; e += 2 * kBwdThreads) {
+                SlotIn in[2];
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int x = e + u * kBwdThreads;
+                    in[u].ok = false;
+                    if (x < m) {
+                        const int sidx = lslot[x];
+                        const int r = (int)__umulhi((uint32_t)sidx, m_row);
+                        const int within = sidx - r * row_slots;
+                        const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
+                        const int gi = by * kBin + r, gj = bx * kBin + col;
+                        load_slot<SETTINGS>(recs, verts, faces, V, F, lface[x], tile0 + (int64_t)r * W * K + within,
+                                            pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash);
+            }
+            __syncthreads();
+        }
+        for (int e = t; e < kHashSize; e += kBwdThreads) {
+            const int32_t vid = hkey[e];
+            if (vid >= 0) {
+                atomicAdd(&grad_verts[3 * (int64_t)vid + 0], from_fixed(hval[e][0]));
+                atomicAdd(&grad_verts[3 * (int64_t)vid + 1], from_fixed(hval[e][1]));
+                atomicAdd(&grad_verts[3 * (int64_t)vid + 2], from_fixed(hval[e][2]));
             }
         }
-        __syncthreads();
-        const int m = min(kListCap, total - chunk);
-        for (int e = t; e < m; e += kBwdThreads) {
-            const int64_t f = lface[e];
-            if (f < 0 || f >= F) continue;
-            const int pl = lslot[e] >> 8, slot = lslot[e] & 0xff;
-            const int gi = by * kBin + pl / kBin, gj = bx * kBin + pl % kBin;
-            FaceRec r;
-            int64_t vi[3];
-            bool ok;
-            if (recs) {
-                r = recs[f];
-                vi[0] = faces[3 * f + 0];
-                vi[1] = faces[3 * f + 1];
-                vi[2] = faces[3 * f + 2];
-                ok = r.face >= 0 || (vi[0] >= 0 && vi[0] < V && vi[1] >= 0 && vi[1] < V && vi[2] >= 0 && vi[2] < V);
-            } else {
-                load_face(verts, faces, f, V, r, vi, ok);
-            }
-            if (!ok) continue;
-            const float px = pixel_centre(gj, W), py = pixel_centre(gi, H);
-            const int64_t so = (((int64_t)n * H + gi) * W + gj) * K + slot;
-            PairState s;
-            eval_pair(r, px, py, __builtin_inff(), true, SETTINGS, s);
-            const float gz = gzb ? gzb[so] : 0.0f;
-            const float gd = gds ? gds[so] : 0.0f;
-            const float gb0 = gba ? gba[3 * so + 0] : 0.0f;
-            const float gb1 = gba ? gba[3 * so + 1] : 0.0f;
-            const float gb2 = gba ? gba[3 * so + 2] : 0.0f;
-            float g[9];
-            slot_partials(r, s, px, py, gz, gb0, gb1, gb2, gd, SETTINGS, g);
-            vertex_add(hkey, hval, grad_verts, vi[0], g[0], g[1], g[2], use_hash);
-            vertex_add(hkey, hval, grad_verts, vi[1], g[3], g[4], g[5], use_hash);
-            vertex_add(hkey, hval, grad_verts, vi[2], g[6], g[7], g[8], use_hash);
-        }
-        __syncthreads();
-    }
-    for (int e = t; e < kHashSize; e += kBwdThreads) {
-        const int32_t vid = hkey[e];
-        if (vid >= 0) {
-            atomicAdd(&grad_verts[3 * (int64_t)vid + 0], from_fixed(hval[e][0]));
-            atomicAdd(&grad_verts[3 * (int64_t)vid + 1], from_fixed(hval[e][1]));
-            atomicAdd(&grad_verts[3 * (int64_t)vid + 2], from_fixed(hval[e][2]));
-        }
-    }
-    __syncthreads();   // the table is cleared for the next tile
+        __syncthreads();   // the table is cleared for the next tile
     }
 }
 
 template <uint32_t SETTINGS>
 static void launch_backward_slots(const BwdArgs& a, bool reuse, const FaceRec* recs, const int32_t* order,
-                                  const int32_t* count, int32_t* queue) {
+                                  const int32_t* count) {
     int64_t grid = a.L.bins;
     if (reuse) {
-        // as many workgroups as stay resident; each takes tiles from the queue
+        // as many workgroups as stay resident; each takes its share of the order
         static int resident_per_cu = 0;
         int dev = 0, cus = 0;
         if (resident_per_cu == 0 &&
@@ -307,7 +332,7 @@ static void launch_backward_slots(const BwdArgs& a, bool reuse, const FaceRec* r
         grid = std::min<int64_t>(grid, resident);
     }
     backward_slots<SETTINGS><<<(unsigned)grid, kBwdThreads, 0, a.stream>>>(
-        recs, order, count, queue, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
+        recs, order, count, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
         (int32_t)a.L.nby, a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
 }
 
@@ -317,13 +342,12 @@ hipError_t launch_backward(const BwdArgs& a) {
     const bool work = npix > 0 && a.F > 0;
     // With the forward's workspace, its per-face records (vertex positions,
     // 1/A, inverse edge lengths) replace the per-slot gathers and divisions,
-    // and its bin order and counts drive a tile queue that skips empty bins.
+    // and its heaviest-first bin order and counts deal the non-empty tiles
+    // to the resident workgroups.
     const bool reuse = a.reuse_forward && work;
-    WsHeader* hdr = reuse ? reinterpret_cast<WsHeader*>(a.ws) : nullptr;
-    int32_t* queue = reuse ? &hdr->bwd_next : nullptr;
     if (n3 > 0) {
         timing_begin(kKZeroGrad, a.stream);
-        zero_f32<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_verts, n3, queue);
+        zero_f32<<<(unsigned)std::min<int64_t>(2048, (n3 + 255) / 256), 256, 0, a.stream>>>(a.grad_verts, n3);
         timing_end(kKZeroGrad, a.stream);
     }
     if (!work) return hipGetLastError();
@@ -333,10 +357,10 @@ hipError_t launch_backward(const BwdArgs& a) {
     constexpr uint32_t kP = DMR_RASTER_PERSPECTIVE_CORRECT, kU = DMR_RASTER_UNCLIPPED_BARY;
     timing_begin(kKBackward, a.stream);
     switch (a.settings & (kP | kU)) {
-        case 0: launch_backward_slots<0>(a, reuse, recs, order, count, queue); break;
-        case kP: launch_backward_slots<kP>(a, reuse, recs, order, count, queue); break;
-        case kU: launch_backward_slots<kU>(a, reuse, recs, order, count, queue); break;
-        default: launch_backward_slots<kP | kU>(a, reuse, recs, order, count, queue); break;
+        case 0: launch_backward_slots<0>(a, reuse, recs, order, count); break;
+        case kP: launch_backward_slots<kP>(a, reuse, recs, order, count); break;
+        case kU: launch_backward_slots<kU>(a, reuse, recs, order, count); break;
+        default: launch_backward_slots<kP | kU>(a, reuse, recs, order, count); break;
     }
     timing_end(kKBackward, a.stream);
     return hipGetLastError();
