@@ -34,25 +34,40 @@ constexpr int kSplitMin = 1024;
 constexpr int kSplitMaxK = 16;
 constexpr int kItemWhole = 4;   // item code: bin << 3 | quarter (0..3) or kItemWhole
 
-// Per-face record written by the setup pass and read by the fine pass
-// (80 bytes, five 16-byte vectors). A face that can never be a candidate
-// (degenerate, all depths <= 0, no pixel centre near it, bad vertex index)
-// has face == -1 and an empty pixel box.
+// Per-face record written by the setup pass and read by the fine and
+// backward passes (64 bytes, four 16-byte vectors): the vertex positions,
+// 1/A, the inverse squared edge lengths, and the vertex indices (-1 when an
+// index is out of range, or when the vertex count does not fit in int32;
+// the backward pass then reads the face array). Which faces can be
+// candidates, and their pixel boxes, are in FaceBin.
 struct alignas(16) FaceRec {
     float x0, y0, x1, y1;
     float x2, y2, z0, z1;
     float z2, invA, il0, il1;      // invA = 1/A; il_e = 1/|edge e|^2, edges (0,1) (1,2) (2,0)
-    float il2, xmin, xmax, ymin;   // closed xy bounding box of the three vertices
-    float ymax;
-    int32_t face;                  // global face index, or -1
-    int32_t box_lo;                // first pixel column | first pixel row << 16
-    int32_t box_hi;                // last pixel column | last pixel row << 16
+    float il2;
+    int32_t v0, v1, v2;
 };
-static_assert(sizeof(FaceRec) == 80, "FaceRec layout");
+static_assert(sizeof(FaceRec) == 64, "FaceRec layout");
 
-// What the binning passes need of a face (16 bytes): its pixel box (as in
-// FaceRec; empty for a face that is never a candidate), its mesh, and the
-// bits of its smallest vertex depth.
+// Closed xy bounding box of the three vertices (exact: min and max round
+// nothing).
+struct FaceBox {
+    float xmin, xmax, ymin, ymax;
+};
+__device__ __forceinline__ FaceBox face_box(const FaceRec& r) {
+    FaceBox b;
+    b.xmin = fminf(r.x0, fminf(r.x1, r.x2));
+    b.xmax = fmaxf(r.x0, fmaxf(r.x1, r.x2));
+    b.ymin = fminf(r.y0, fminf(r.y1, r.y2));
+    b.ymax = fmaxf(r.y0, fmaxf(r.y1, r.y2));
+    return b;
+}
+
+// What the binning passes need of a face (16 bytes): its pixel box (first
+// column | first row << 16, last column | last row << 16; empty, lo > hi,
+// for a face that is never a candidate: degenerate, all depths <= 0, no
+// pixel centre near it, bad vertex index), its mesh, and the bits of its
+// smallest vertex depth.
 struct alignas(16) FaceBin {
     int32_t box_lo, box_hi;
     int32_t mesh;
@@ -185,7 +200,8 @@ __device__ __forceinline__ void eval_pair(const FaceRec& r, float px, float py, 
     s.b0 = w0 * r.invA;
     s.b1 = w1 * r.invA;
     s.b2 = w2 * r.invA;
-    bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    const FaceBox bb = face_box(r);
+    bool in_box = (px >= bb.xmin) && (px <= bb.xmax) && (py >= bb.ymin) && (py <= bb.ymax);
     s.inside = in_box && (s.b0 > 0.0f) && (s.b1 > 0.0f) && (s.b2 > 0.0f);
     s.d2 = 0.0f;
     s.argmin = 0;

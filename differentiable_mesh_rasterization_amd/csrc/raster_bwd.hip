@@ -49,10 +49,7 @@ __device__ __forceinline__ void load_face(const float* __restrict__ verts, const
     r.il1 = 1.0f / (ux * ux + uy * uy);
     ux = r.x0 - r.x2; uy = r.y0 - r.y2;
     r.il2 = 1.0f / (ux * ux + uy * uy);
-    r.xmin = fminf(r.x0, fminf(r.x1, r.x2));
-    r.xmax = fmaxf(r.x0, fmaxf(r.x1, r.x2));
-    r.ymin = fminf(r.y0, fminf(r.y1, r.y2));
-    r.ymax = fmaxf(r.y0, fmaxf(r.y1, r.y2));
+    r.v0 = r.v1 = r.v2 = -1;
 }
 
 // Backward of the perspective weighting o = n / D, n_k = a_k z_{k+1} z_{k+2}
@@ -164,12 +161,19 @@ __device__ __forceinline__ void load_slot(const FaceRec* __restrict__ recs, cons
     in.ok = f >= 0 && f < F;
     if (!in.ok) return;
     if (recs) {
+        // the record carries the vertex indices unless one is out of range
+        // or they do not fit in int32
         in.r = recs[f];
-        in.vi[0] = faces[3 * f + 0];
-        in.vi[1] = faces[3 * f + 1];
-        in.vi[2] = faces[3 * f + 2];
-        in.ok = in.r.face >= 0 || (in.vi[0] >= 0 && in.vi[0] < V && in.vi[1] >= 0 && in.vi[1] < V && in.vi[2] >= 0 &&
-                                   in.vi[2] < V);
+        if (in.r.v0 >= 0) {
+            in.vi[0] = in.r.v0;
+            in.vi[1] = in.r.v1;
+            in.vi[2] = in.r.v2;
+        } else {
+            in.vi[0] = faces[3 * f + 0];
+            in.vi[1] = faces[3 * f + 1];
+            in.vi[2] = faces[3 * f + 2];
+            in.ok = in.vi[0] >= 0 && in.vi[0] < V && in.vi[1] >= 0 && in.vi[1] < V && in.vi[2] >= 0 && in.vi[2] < V;
+        }
     } else {
         load_face(verts, faces, f, V, in.r, in.vi, in.ok);
     }

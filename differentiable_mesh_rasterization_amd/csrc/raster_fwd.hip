@@ -81,9 +81,7 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     bool live = false;
     if (f < F) {
         FaceRec r;
-        r.face = -1;
-        r.box_lo = 0x7fff7fff;  // empty box: lo > hi
-        r.box_hi = 0;
+        int32_t box_lo = 0x7fff7fff, box_hi = 0;   // empty box: lo > hi
         // the faces of a block nearly always belong to the mesh of its first
         const bool in_home = home_lo <= f && f < home_hi;
         const int64_t n = in_home ? home : mesh_of(off, N, f);
@@ -91,6 +89,10 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         int64_t vi0 = faces[3 * f + 0], vi1 = faces[3 * f + 1], vi2 = faces[3 * f + 2];
         bool idx_ok = vi0 >= 0 && vi0 < V && vi1 >= 0 && vi1 < V && vi2 >= 0 && vi2 < V;
         if (!idx_ok) atomicOr(&hdr->flags, DMR_FLAG_BAD_VERTEX_INDEX);
+        const bool ids32 = idx_ok && V <= (int64_t)INT32_MAX;
+        r.v0 = ids32 ? (int32_t)vi0 : -1;
+        r.v1 = ids32 ? (int32_t)vi1 : -1;
+        r.v2 = ids32 ? (int32_t)vi2 : -1;
         float x0 = 0, y0 = 0, z0 = 0, x1 = 0, y1 = 0, z1 = 0, x2 = 0, y2 = 0, z2 = 0;
         if (idx_ok) {
             x0 = verts[3 * vi0]; y0 = verts[3 * vi0 + 1]; z0 = verts[3 * vi0 + 2];
@@ -117,7 +119,6 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         }
         float xmin = fminf(x0, fminf(x1, x2)), xmax = fmaxf(x0, fmaxf(x1, x2));
         float ymin = fminf(y0, fminf(y1, y2)), ymax = fmaxf(y0, fmaxf(y1, y2));
-        r.xmin = xmin; r.xmax = xmax; r.ymin = ymin; r.ymax = ymax;
         const bool back = (settings & DMR_RASTER_CULL_BACKFACES) && A > 0.0f;
         if (ok && idx_ok && A != 0.0f && zpos && !back) {
             // Conservative pixel box: the face's box grown by the blur radius
@@ -137,9 +138,8 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
             ih = fminf(ih, (float)(H - 1));
             if (jl <= jh && il <= ih) {
                 int j0 = (int)jl, j1 = (int)jh, i0 = (int)il, i1 = (int)ih;
-                r.face = (int32_t)f;
-                r.box_lo = j0 | (i0 << 16);
-                r.box_hi = j1 | (i1 << 16);
+                box_lo = j0 | (i0 << 16);
+                box_hi = j1 | (i1 << 16);
                 live = true;
                 const bool local = use_lds && n == home;
                 int32_t* cnt = bin_count + n * per_img;
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
         }
         recs[f] = r;
         FaceBin fb;
-        fb.box_lo = r.box_lo;
-        fb.box_hi = r.box_hi;
+        fb.box_lo = box_lo;
+        fb.box_hi = box_hi;
         fb.mesh = (int32_t)n;
         fb.zmin_bits = __float_as_uint(fminf(z0, fminf(z1, z2)));
         fbin[f] = fb;
@@ -573,7 +573,8 @@ __device__ __forceinline__ float edge_dist2(float dxa, float dya, float ux, floa
 // wave evaluate unrelated pairs, and most pairs lie outside their triangle
 // and need the three edge distances anyway.
 template <bool PERSP>
-__device__ __forceinline__ double pair_key(const FaceRec& r, float px, float py, float blur, double bound) {
+__device__ __forceinline__ double pair_key(const FaceRec& r, int32_t face, float px, float py, float blur,
+                                           double bound) {
     const float dx0 = r.x0 - px, dy0 = r.y0 - py;
     const float dx1 = r.x1 - px, dy1 = r.y1 - py;
     const float dx2 = r.x2 - px, dy2 = r.y2 - py;
@@ -581,7 +582,8 @@ __device__ __forceinline__ double pair_key(const FaceRec& r, float px, float py,
     const float w1 = dx2 * dy0 - dy2 * dx0;
     const float w2 = dx0 * dy1 - dy0 * dx1;
     const float b0 = w0 * r.invA, b1 = w1 * r.invA, b2 = w2 * r.invA;
-    const bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    const FaceBox bb = face_box(r);
+    const bool in_box = (px >= bb.xmin) && (px <= bb.xmax) && (py >= bb.ymin) && (py <= bb.ymax);
     const bool inside = in_box && (b0 > 0.0f) && (b1 > 0.0f) && (b2 > 0.0f);
     float c0 = b0 < 0.0f ? 0.0f : b0;
     float c1 = b1 < 0.0f ? 0.0f : b1;
@@ -608,7 +610,7 @@ __device__ __forceinline__ double pair_key(const FaceRec& r, float px, float py,
     d = d2 < d ? d2 : d;
     // outside the triangle, d < blur fails for every blur <= 0 (d >= 0)
     const bool cand = (inside || d < blur) && (z > 0.0f);
-    const double kk = make_key(z, r.face);
+    const double kk = make_key(z, face);
     return (cand && kk < bound) ? kk : empty_key();
 }
 
@@ -626,7 +628,8 @@ __device__ __forceinline__ void slot_outputs(const FaceRec& r, float px, float p
     const float w1 = dx2 * dy0 - dy2 * dx0;
     const float w2 = dx0 * dy1 - dy0 * dx1;
     const float b0 = w0 * r.invA, b1 = w1 * r.invA, b2 = w2 * r.invA;
-    const bool in_box = (px >= r.xmin) && (px <= r.xmax) && (py >= r.ymin) && (py <= r.ymax);
+    const FaceBox bb = face_box(r);
+    const bool in_box = (px >= bb.xmin) && (px <= bb.xmax) && (py >= bb.ymin) && (py <= bb.ymax);
     const bool inside = in_box && (b0 > 0.0f) && (b1 > 0.0f) && (b2 > 0.0f);
     float c0 = b0 < 0.0f ? 0.0f : b0;
     float c1 = b1 < 0.0f ? 0.0f : b1;
@@ -753,10 +756,14 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, uint32_t settings, int32_t nbx, int32_t nby,
     int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
     float* __restrict__ dists) {
-    __shared__ FaceRec srec[kFineThreads];
+    // staged face records, their face indices and the owners' records; the
+    // output phase reuses the whole block for its key exchange
+    __shared__ __align__(16) unsigned char stage[kFineThreads * (sizeof(FaceRec) + 4 + sizeof(OwnerRec))];
+    FaceRec* srec = reinterpret_cast<FaceRec*>(stage);
+    int32_t* sface = reinterpret_cast<int32_t*>(stage + kFineThreads * sizeof(FaceRec));
+    OwnerRec* orec = reinterpret_cast<OwnerRec*>(stage + kFineThreads * (sizeof(FaceRec) + 4));
     // the round's masks
     __shared__ __align__(16) unsigned char aux[2 * kBin * (kFineThreads / 64) * 8];
-    __shared__ OwnerRec orec[kFineThreads];
     __shared__ uint16_t pcode[kPairWin];
     __shared__ double pres[kPairWin];
     __shared__ int32_t ofill[kFineThreads];
@@ -843,7 +850,10 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 r0 = max((fb.box_lo >> 16) - by * kBin, reg_r);
                 r1 = min((fb.box_hi >> 16) - by * kBin, reg_r + reg_w - 1);
                 live = (c0 <= c1) && (r0 <= r1);
-                if (live) srec[t] = recs[fid];
+                if (live) {
+                    srec[t] = recs[fid];
+                    sface[t] = (int32_t)fid;
+                }
             }
 #pragma unroll
             for (int c = 0; c < kBin; ++c) {
@@ -905,7 +915,8 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 for (int e = t; e < wtotal; e += kFineThreads) {
                     const uint32_t pc = pcode[e];
                     const OwnerRec ow = orec[pc >> 8];
-                    const double kk = pair_key<PERSP>(srec[pc & 255u], ow.px, ow.py, blur, ow.bound);
+                    const double kk =
+                        pair_key<PERSP>(srec[pc & 255u], sface[pc & 255u], ow.px, ow.py, blur, ow.bound);
                     if (key_bits(kk) != kEmptyKeyBits) pres[atomicAdd(&ofill[pc >> 8], 1)] = kk;
                 }
                 __syncthreads();
@@ -922,16 +933,16 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             merge_with_lane<KMAX>(key, 2);
         }
 
-        // ---- output: exchange keys through LDS (reusing srec); write each
-        // region row's reg_w*K slots with consecutive lanes on consecutive
-        // slots (indices, depths and the padding of empty slots), collecting
-        // the filled slots in a list (reusing the pair buffers); then
-        // evaluate the listed slots densely for their barycentrics and
-        // distances.
-        uint64_t* kbuf = reinterpret_cast<uint64_t*>(srec);
-        constexpr int kBufKeys = (int)(sizeof(srec) / (sizeof(uint64_t)));
+        // ---- output: exchange keys through LDS (reusing the staging
+        // block); write each region row's reg_w*K slots with consecutive
+        // lanes on consecutive slots (indices, depths and the padding of
+        // empty slots), collecting the filled slots in a list (reusing the
+        // pair buffers); then evaluate the listed slots densely for their
+        // barycentrics and distances.
+        uint64_t* kbuf = reinterpret_cast<uint64_t*>(stage);
+        constexpr int kBufKeys = (int)sizeof(stage) / (int)sizeof(uint64_t);
         uint16_t* olist = reinterpret_cast<uint16_t*>(pres);
-        constexpr int kOutList = (int)(sizeof(pres) / sizeof(uint16_t));
+        constexpr int kOutList = (int)sizeof(pres) / (int)sizeof(uint16_t);
         const int row_slots = reg_w * K;
         const int rows_per_pass = max(1, min(reg_w, min(kBufKeys, kOutList) / row_slots));
         const bool writer = !quarter || sub == 0;
