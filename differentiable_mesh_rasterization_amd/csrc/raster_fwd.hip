@@ -746,7 +746,7 @@ struct OwnerRec {
 // The K output slots of each row of the item's region are then written
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
-constexpr int kPairWin = 1024;
+constexpr int kPairWin = 1536;
 
 template <int KMAX, bool PERSP>
 __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 4 : 1, 8))) void fine_raster(
