@@ -22,10 +22,20 @@ constexpr int kBinPixels = kBin * kBin;
 constexpr int kFineThreads = kBinPixels;
 // Faces per setup/fill workgroup.
 constexpr int kSetupThreads = 256;
-// Bin lists up to kSortMax faces are ordered by depth lower bound; each
-// such list has kSortMax / kFineThreads per-round depth bounds.
+// Bin lists of more than one round and up to kSortMax faces are ordered by
+// depth lower bound; each such list has kSortMax / kFineThreads per-round
+// depth bounds. A list of one round (at most kSortMin entries) is left as
+// it is: the fine passes evaluate a round's faces all together, so their
+// order changes nothing, and no earlier round could end the list.
 constexpr int kSortMax = 4096;
+constexpr int kSortMin = kFineThreads;
 constexpr int kRoundsPerBin = kSortMax / kFineThreads;
+
+// Whether a bin list (offset o, cnt entries) is in the workspace and
+// depth-sorted with round bounds.
+__host__ __device__ __forceinline__ bool list_sorted(int64_t o, int32_t cnt, int64_t capacity) {
+    return o + cnt <= capacity && cnt > kSortMin && cnt <= kSortMax;
+}
 // The fine pass takes its work from a queue of items, heaviest first. A bin
 // with at least kSplitMin faces becomes four items, one per 8x8 quarter,
 // each worked by four lanes per pixel (for K <= kSplitMaxK); any other bin

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
     const bool list_mode = o + cnt <= capacity;
-    const bool sorted = list_mode && cnt <= kSortMax;
+    const bool sorted = list_sorted(o, cnt, capacity);
     const float* lb = round_lb + b * kRoundsPerBin;
     int64_t f0 = off[n], f1 = off[n + 1];
     f0 = f0 < 0 ? 0 : f0;

@@ -437,10 +437,7 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
     const int64_t o = offset[b];
     const int t = threadIdx.x;
     float* lb = round_lb + b * kRoundsPerBin;
-    if (cnt == 0 || o + cnt > capacity || cnt > kSortMax) {
-        if (t < kRoundsPerBin) lb[t] = -__builtin_inff();
-        return;
-    }
+    if (!list_sorted(o, cnt, capacity)) return;   // the fine passes read no bound of it
     if (t == 0) {
         lo_s = 0xffffffffu;
         hi_s = 0u;
@@ -817,7 +814,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         const int32_t cnt = count[b];
         const int64_t o = offset[b];
         const bool list_mode = (o + cnt <= capacity);
-        const bool sorted = list_mode && cnt <= kSortMax;
+        const bool sorted = list_sorted(o, cnt, capacity);
         const float* lb = round_lb + b * kRoundsPerBin;
         int64_t f0 = off[n], f1 = off[n + 1];
         f0 = f0 < 0 ? 0 : f0;
