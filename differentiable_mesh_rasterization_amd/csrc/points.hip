@@ -138,18 +138,22 @@ hipError_t launch_point_setup(const FwdArgs& a, PointRec* recs, FaceBin* fbin, i
 // fine pass
 // ---------------------------------------------------------------------------
 
-// Sorted insertion of key k into key[0..KMAX) (ascending; ~0 marks empty).
+// Keys: (z bits << 32) | point index with z > 0. Read as binary64 such a
+// pattern is finite, non-negative and not a NaN, and numeric order is
+// pattern order, so one v_min_f64 / v_max_f64 moves a key one slot (+inf
+// marks an empty slot); written out because the compiler's fmin/fmax first
+// quiet their operands.
+constexpr uint64_t kPointEmptyBits = 0x7ff0000000000000ull;
+
 template <int KMAX>
-__device__ __forceinline__ void point_topk_insert(uint64_t (&key)[KMAX], uint64_t k) {
-    bool lt[KMAX];
+__device__ __forceinline__ void point_topk_push(double (&key)[KMAX], double k) {
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) lt[q] = k < key[q];
-#pragma unroll
-    for (int q = KMAX - 1; q > 0; --q) {
-        const uint64_t from = lt[q - 1] ? key[q - 1] : k;
-        key[q] = lt[q] ? from : key[q];
+    for (int q = 0; q < KMAX; ++q) {
+        double hi;
+        asm("v_max_f64 %0, %1, %2" : "=v"(hi) : "v"(key[q]), "v"(k));
+        asm("v_min_f64 %0, %0, %1" : "+v"(key[q]) : "v"(k));
+        k = hi;
     }
-    key[0] = lt[0] ? k : key[0];
 }
 
 // Squared distance of the pixel centre to the point, in the fixed order.
@@ -168,8 +172,9 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     __shared__ PointRec spt[kPointThreads];
     __shared__ uint64_t colmask[kBin][kPointThreads / 64];
     __shared__ uint64_t rowmask[kBin][kPointThreads / 64];
-    constexpr int kBufKeys = 1024;
+    constexpr int kBufKeys = 2560;   // one pass for K <= 10
     __shared__ uint64_t kbuf[kBufKeys];
+    __shared__ float pcx[kBin], pcy[kBin];   // pixel centres of the bin's columns and rows
     const int t = threadIdx.x;
     const int lane = t & 63, wave = t >> 6;
     if ((int64_t)blockIdx.x >= (int64_t)hdr->fine_items) return;
@@ -184,10 +189,12 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     const int i = by * kBin + il, j = bx * kBin + jl;
     const bool valid = i < H && j < W;
     const float px = pixel_centre(j, W), py = pixel_centre(i, H);
+    if (t < kBin) pcx[t] = pixel_centre(bx * kBin + t, W);
+    else if (t < 2 * kBin) pcy[t - kBin] = pixel_centre(by * kBin + t - kBin, H);
 
-    uint64_t key[KMAX];
+    double key[KMAX];
 #pragma unroll
-    for (int q = 0; q < KMAX; ++q) key[q] = ~0ull;
+    for (int q = 0; q < KMAX; ++q) key[q] = __longlong_as_double((long long)kPointEmptyBits);
 
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
@@ -203,7 +210,8 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     for (int64_t base = 0; base < total; base += kPointThreads) {
         // every point from this round on has z >= lb[round]
         if (sorted && !done) {
-            if (lb[base / kPointThreads] > __uint_as_float((uint32_t)(key[KMAX - 1] >> 32))) done = true;
+            const uint64_t last = (uint64_t)__double_as_longlong(key[KMAX - 1]);
+            if (lb[base / kPointThreads] > __uint_as_float((uint32_t)(last >> 32))) done = true;
         }
         if (__syncthreads_count(!done) == 0) break;
         const int64_t q = base + t;
@@ -238,8 +246,8 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
                     m &= m - 1;
                     const PointRec r = spt[u];
                     if (point_d2(px, py, r.x, r.y) < r2) {
-                        const uint64_t kk = ((uint64_t)__float_as_uint(r.z) << 32) | (uint32_t)r.idx;
-                        if (kk < key[KMAX - 1]) point_topk_insert<KMAX>(key, kk);
+                        const double kk = __hiloint2double((int)__float_as_uint(r.z), r.idx);
+                        if (kk < key[KMAX - 1]) point_topk_push<KMAX>(key, kk);
                     }
                 }
             }
@@ -252,6 +260,10 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     const int row_slots = kBin * K;
     const int rows_per_pass = max(1, min(kBin, kBufKeys / row_slots));
     const int64_t row0 = ((int64_t)n * H + by * kBin) * W + bx * kBin;
+    // slot e -> (row, slot within the row, column): divisions by
+    // multiplication (exact while e * divisor < 2^32)
+    const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
+    const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
     for (int ra = 0; ra < kBin; ra += rows_per_pass) {
         const int rb = min(kBin, ra + rows_per_pass);
         __syncthreads();
@@ -259,19 +271,19 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
             uint64_t* dst = kbuf + ((il - ra) * kBin + jl) * K;
 #pragma unroll
             for (int q = 0; q < KMAX; ++q)
-                if (q < K) dst[q] = key[q];
+                if (q < K) dst[q] = (uint64_t)__double_as_longlong(key[q]);
         }
         __syncthreads();
         const int npass = (rb - ra) * row_slots;
         for (int e = t; e < npass; e += kPointThreads) {
-            const int rr = e / row_slots;
+            const int rr = (int)__umulhi((uint32_t)e, m_row);
             const int within = e - rr * row_slots;
-            const int jj = within / K;
+            const int jj = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
             const int gi = by * kBin + ra + rr, gj = bx * kBin + jj;
             if (gi >= H || gj >= W) continue;
             const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
             const uint64_t kk = kbuf[e];
-            if (kk == ~0ull) {
+            if (kk == kPointEmptyBits) {
                 out_idx[so] = -1;
                 zbuf[so] = -1.0f;
                 dists[so] = -1.0f;
@@ -280,7 +292,7 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
                 const PointRec r = recs[pid];
                 out_idx[so] = pid;
                 zbuf[so] = __uint_as_float((uint32_t)(kk >> 32));
-                dists[so] = point_d2(pixel_centre(gj, W), pixel_centre(gi, H), r.x, r.y);
+                dists[so] = point_d2(pcx[jj], pcy[ra + rr], r.x, r.y);
             }
         }
     }
