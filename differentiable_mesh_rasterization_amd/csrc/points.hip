@@ -227,14 +227,14 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
             live = c0 <= c1 && r0 <= r1;
             if (live) spt[t] = recs[pid];
         }
+        // the point's columns and rows as bit sets; ballot c of them is the
+        // wave's mask for bin column (row) c (every lane writes the same value)
+        const uint32_t colbits = live ? (((2u << c1) - 1u) & ~((1u << c0) - 1u)) : 0u;
+        const uint32_t rowbits = live ? (((2u << r1) - 1u) & ~((1u << r0) - 1u)) : 0u;
 #pragma unroll
         for (int c = 0; c < kBin; ++c) {
-            const uint64_t mc = __ballot(live && c0 <= c && c <= c1);
-            const uint64_t mr = __ballot(live && r0 <= c && c <= r1);
-            if (lane == 0) {
-                colmask[c][wave] = mc;
-                rowmask[c][wave] = mr;
-            }
+            colmask[c][wave] = __ballot((colbits >> c) & 1u);
+            rowmask[c][wave] = __ballot((rowbits >> c) & 1u);
         }
         __syncthreads();
         if (!done) {
