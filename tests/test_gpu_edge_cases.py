@@ -2,7 +2,8 @@
 beyond the candidate count, culled and degenerate faces, exact depth ties,
 pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
-thousands of faces in one bin, heavy bins split into quarter items, faces
+thousands of faces in one bin, heavy bins split into quarter items, hundreds
+of faces each covering every pixel (whole and split bins), faces
 using another mesh's vertices, the largest image side, hundreds of small
 meshes, invalid vertex indices, and the hand-worked cases."""
 
@@ -175,6 +176,33 @@ def dense_split_bins_on_ragged_edge():
     # split bins in the last bin row and column, partly outside the image
     v, f = _soup(19, 2500, lo=0.75, hi=1.0, sigma=0.02)
     return v, f, [0, 2500], 37, 45, 16, 5e-4
+
+
+def _covering(seed, F):
+    """F large triangles that each cover the whole image, with depths spread
+    over [0.5, 3] per vertex, so that depth bounds prune little."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    base = np.array([[-3.0, -3.0], [5.0, -3.0], [-3.0, 5.0]])
+    xy = base[None] + rng.uniform(-0.3, 0.3, (F, 3, 2))
+    z = rng.uniform(0.5, 3.0, (F, 3, 1))
+    v = np.concatenate([xy, z], 2).reshape(-1, 3)
+    return v.astype(np.float32), np.arange(3 * F).reshape(F, 3)
+
+
+@case
+def all_faces_cover_every_pixel():
+    # every pixel has every staged face as a candidate: 256 pairs per pixel
+    # per round, many pair windows per round
+    v, f = _covering(20, 700)
+    return v, f, [0, 700], 32, 32, 12, 1e-3
+
+
+@case
+def all_faces_cover_a_split_bin():
+    # 1,200 faces over one bin: four quarter items, four owners per pixel,
+    # each with 64 candidates per round
+    v, f = _covering(21, 1200)
+    return v, f, [0, 1200], 16, 16, 10, 1e-4
 
 
 @case
