@@ -3,7 +3,8 @@ beyond the candidate count, culled and degenerate faces, exact depth ties,
 pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
 thousands of faces in one bin, heavy bins split into quarter items, hundreds
-of faces each covering every pixel (whole and split bins), faces
+of faces each covering every pixel (whole and split bins), subnormal depths,
+faces
 using another mesh's vertices, the largest image side, hundreds of small
 meshes, invalid vertex indices, and the hand-worked cases."""
 
@@ -203,6 +204,16 @@ def all_faces_cover_a_split_bin():
     # each with 64 candidates per round
     v, f = _covering(21, 1200)
     return v, f, [0, 1200], 16, 16, 10, 1e-4
+
+
+@case
+def tiny_positive_depths():
+    # depths down to binary32 subnormals: their keys read as binary64 are
+    # subnormal too, and must still order exactly
+    rng = np.random.Generator(np.random.PCG64(22))
+    v, f = _soup(22, 300, sigma=0.08)
+    v[:, 2] = (rng.uniform(1.0, 2.0, len(v)) * 10.0 ** rng.integers(-44, -36, len(v))).astype(np.float32)
+    return v, f, [0, 300], 24, 20, 8, 1e-3
 
 
 @case
