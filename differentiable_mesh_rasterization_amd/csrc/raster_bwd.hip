@@ -144,6 +144,76 @@ __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState&
 constexpr int kBwdThreads = kBin * kBin;
 constexpr int kListCap = 1024;   // tile slots read (and at most compacted) per chunk
 
+// Records of the four slots of a lane quad, loaded cooperatively: in load k
+// lane p of the quad fetches the 16-byte piece p of slot k's record, so each
+// load instruction reads whole 64-byte records (one cache request per
+// record instead of four), and a 4x4 transpose within the quad (two rounds
+// of quad permutations) leaves every lane with its own slot's record. All
+// lanes of the wave must take part; `f` is this lane's face, or any valid
+// face index when the lane has no slot.
+template <int CTRL>
+__device__ __forceinline__ int quad_perm(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ FaceRec quad_load_record(const FaceRec* __restrict__ recs, int32_t f) {
+    const int p = threadIdx.x & 3;
+    // faces of the quad's four slots
+    int32_t fq[4];
+    fq[0] = quad_perm<0x00>(f);
+    fq[1] = quad_perm<0x55>(f);
+    fq[2] = quad_perm<0xaa>(f);
+    fq[3] = quad_perm<0xff>(f);
+    // w[4k + c] = dword c of piece p of slot k's record
+    int w[16];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int4 v = reinterpret_cast<const int4*>(recs + fq[k])[p];
+        w[4 * k + 0] = v.x;
+        w[4 * k + 1] = v.y;
+        w[4 * k + 2] = v.z;
+        w[4 * k + 3] = v.w;
+    }
+    // transpose: afterwards w[4k + c] = dword c of piece k of this lane's
+    // slot. Round b takes, where lane bit b and piece bit b differ, the
+    // element of piece k ^ 2^b held by lane p ^ 2^b.
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int bit = 1 << b;
+        int t[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool take = ((p ^ k) & bit) != 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int o = w[4 * (k ^ bit) + c];
+                const int x = b == 0 ? quad_perm<0xb1>(o) : quad_perm<0x4e>(o);
+                t[4 * k + c] = take ? x : w[4 * k + c];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = t[i];
+    }
+    static_assert(sizeof(FaceRec) == 64, "record of four pieces");
+    FaceRec r;
+    r.x0 = __int_as_float(w[0]);
+    r.y0 = __int_as_float(w[1]);
+    r.x1 = __int_as_float(w[2]);
+    r.y1 = __int_as_float(w[3]);
+    r.x2 = __int_as_float(w[4]);
+    r.y2 = __int_as_float(w[5]);
+    r.z0 = __int_as_float(w[6]);
+    r.z1 = __int_as_float(w[7]);
+    r.z2 = __int_as_float(w[8]);
+    r.invA = __int_as_float(w[9]);
+    r.il0 = __int_as_float(w[10]);
+    r.il1 = __int_as_float(w[11]);
+    r.il2 = __int_as_float(w[12]);
+    r.v0 = w[13];
+    r.v1 = w[14];
+    r.v2 = w[15];
+    return r;
+}
+
 // One filled slot's inputs, loaded ahead of its evaluation.
 struct SlotIn {
     FaceRec r;
@@ -153,17 +223,17 @@ struct SlotIn {
     float gz, gd, gb0, gb1, gb2;
 };
 
-template <uint32_t SETTINGS>
-__device__ __forceinline__ void load_slot(const FaceRec* __restrict__ recs, const float* __restrict__ verts,
-                                          const int64_t* __restrict__ faces, int64_t V, int64_t F, int64_t f,
-                                          int64_t so, float px, float py, const float* __restrict__ gzb,
-                                          const float* __restrict__ gba, const float* __restrict__ gds, SlotIn& in) {
-    in.ok = f >= 0 && f < F;
+// The rest of a slot's inputs once its record is in `in.r` (with the
+// forward's records; `in.ok` says whether the slot has a valid face).
+__device__ __forceinline__ void load_slot_rest(const FaceRec* __restrict__ recs, const float* __restrict__ verts,
+                                               const int64_t* __restrict__ faces, int64_t V, int64_t f, int64_t so,
+                                               float px, float py, const float* __restrict__ gzb,
+                                               const float* __restrict__ gba, const float* __restrict__ gds,
+                                               SlotIn& in) {
     if (!in.ok) return;
     if (recs) {
         // the record carries the vertex indices unless one is out of range
         // or they do not fit in int32
-        in.r = recs[f];
         if (in.r.v0 >= 0) {
             in.vi[0] = in.r.v0;
             in.vi[1] = in.r.v1;
@@ -210,7 +280,8 @@ __device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsi
 // all loads of a chunk in flight together); the filled ones are compacted
 // into an LDS list (their order is free: the LDS sums are exact), and each
 // thread evaluates the list's slots two at a time, the second slot's loads
-// issued with the first's.
+// issued with the first's. The face records are loaded a lane quad at a
+// time (quad_load_record).
 template <uint32_t SETTINGS>
 __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const FaceRec* __restrict__ recs, const int32_t* __restrict__ bin_order, const int32_t* __restrict__ bin_count,
@@ -284,20 +355,28 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
             }
             __syncthreads();
             const int m = nlist;
-            for (int e = t; e < m; e += 2 * kBwdThreads) {
+            // (a trip count uniform over the workgroup: every lane takes part
+            // in the cooperative record loads; a lane without a slot loads
+            // the list's last face, so that no one address is shared by the
+            // idle lanes of every workgroup)
+            const int32_t f_last = m > 0 ? lface[m - 1] : 0;
+            const int32_t f_idle = (f_last >= 0 && (int64_t)f_last < F) ? f_last : 0;
+            for (int e0 = 0; e0 < m; e0 += 2 * kBwdThreads) {
                 SlotIn in[2];
 #pragma unroll
                 for (int u = 0; u < 2; ++u) {
-                    const int x = e + u * kBwdThreads;
-                    in[u].ok = false;
+                    const int x = e0 + t + u * kBwdThreads;
+                    const int64_t f = x < m ? (int64_t)lface[x] : -1;
+                    in[u].ok = f >= 0 && f < F;
+                    if (recs) in[u].r = quad_load_record(recs, in[u].ok ? (int32_t)f : f_idle);
                     if (x < m) {
                         const int sidx = lslot[x];
                         const int r = (int)__umulhi((uint32_t)sidx, m_row);
                         const int within = sidx - r * row_slots;
                         const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
                         const int gi = by * kBin + r, gj = bx * kBin + col;
-                        load_slot<SETTINGS>(recs, verts, faces, V, F, lface[x], tile0 + (int64_t)r * W * K + within,
-                                            pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
+                        load_slot_rest(recs, verts, faces, V, f, tile0 + (int64_t)r * W * K + within,
+                                       pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
                     }
                 }
 #pragma unroll
