@@ -200,10 +200,10 @@ def all_faces_cover_every_pixel():
 
 @case
 def all_faces_cover_a_split_bin():
-    # 1,200 faces over one bin: four quarter items, four owners per pixel,
+    # 2,400 faces over one bin: four quarter items, four owners per pixel,
     # each with 64 candidates per round
-    v, f = _covering(21, 1200)
-    return v, f, [0, 1200], 16, 16, 10, 1e-4
+    v, f = _covering(21, 2400)
+    return v, f, [0, 2400], 16, 16, 10, 1e-4
 
 
 @case
