@@ -142,7 +142,7 @@ __device__ __forceinline__ void slot_partials(const FaceRec& r, const PairState&
 }
 
 constexpr int kBwdThreads = kBin * kBin;
-constexpr int kListCap = 1024;   // tile slots read (and at most compacted) per chunk
+constexpr int kListCap = 1536;   // tile slots read (and at most compacted) per chunk
 
 // Records of the four slots of a lane quad, loaded cooperatively: in load k
 // lane p of the quad fetches the 16-byte piece p of slot k's record, so each
@@ -277,8 +277,9 @@ __device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsi
 // variant carries only its own arithmetic.
 //
 // A tile's slots are read slot-linearly in chunks of kListCap (coalesced,
-// all loads of a chunk in flight together); the filled ones are compacted
-// into an LDS list (their order is free: the LDS sums are exact), and each
+// all loads of a chunk in flight together, and the next chunk's issued
+// before this one is evaluated); the filled ones are compacted into an LDS
+// list (their order is free: the LDS sums are exact), and each
 // thread evaluates the list's slots two at a time, the second slot's loads
 // issued with the first's. The face records are loaded a lane quad at a
 // time (quad_load_record).
@@ -305,94 +306,118 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
     const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
     const int tile_slots = kBin * row_slots;
-    for (int64_t round = 0;; ++round) {
-        const int64_t idx = round * G + ((round & 1) ? G - 1 - blockIdx.x : blockIdx.x);
-        if (idx >= bins) break;
+    // tile of round r (false past the last one)
+    struct Tile {
+        int64_t tile0;
+        int by, bx, rows, cols;
+    };
+    auto tile_at = [&](int64_t r, Tile& T) -> bool {
+        const int64_t idx = r * G + ((r & 1) ? G - 1 - blockIdx.x : blockIdx.x);
+        if (idx >= bins) return false;
         int64_t b = idx;
         if (bin_order) {
             b = bin_order[idx];
-            if (bin_count[b] == 0) break;
+            if (bin_count[b] == 0) return false;
         }
         const int64_t n = b / per_img;
         const int rem = (int)(b - n * per_img);
-        const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
-        const int rows = min(kBin, H - by * kBin), cols = min(kBin, W - bx * kBin);
-        const int64_t tile0 = (((int64_t)n * H + by * kBin) * W + bx * kBin) * K;
-        for (int e = t; e < kHashSize; e += kBwdThreads) {
-            hkey[e] = -1;
-            hval[e][0] = 0;
-            hval[e][1] = 0;
-            hval[e][2] = 0;
-        }
-        for (int cbase = 0; cbase < tile_slots; cbase += kListCap) {
-            if (t == 0) nlist = 0;
-            __syncthreads();
-            int64_t fv[kListCap / kBwdThreads];
+        T.by = rem / nbx;
+        T.bx = rem - T.by * nbx;
+        T.rows = min(kBin, H - T.by * kBin);
+        T.cols = min(kBin, W - T.bx * kBin);
+        T.tile0 = (((int64_t)n * H + T.by * kBin) * W + T.bx * kBin) * K;
+        return true;
+    };
+    constexpr int kPer = kListCap / kBwdThreads;
+    // the chunk's face ids (-1 outside the image or past the tile)
+    auto load_chunk = [&](const Tile& T, int cbase, int64_t (&fv)[kPer]) {
 #pragma unroll
-            for (int q = 0; q < kListCap / kBwdThreads; ++q) {
-                const int sidx = cbase + q * kBwdThreads + t;
-                fv[q] = -1;
-                if (sidx < tile_slots) {
+        for (int q = 0; q < kPer; ++q) {
+            const int sidx = cbase + q * kBwdThreads + t;
+            fv[q] = -1;
+            if (sidx < tile_slots) {
+                const int r = (int)__umulhi((uint32_t)sidx, m_row);
+                const int within = sidx - r * row_slots;
+                const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
+                if (r < T.rows && col < T.cols) fv[q] = pix_to_face[T.tile0 + (int64_t)r * W * K + within];
+            }
+        }
+    };
+    Tile cur;
+    int64_t round = 0;
+    if (!tile_at(round, cur)) return;
+    clear_table(hkey, hval, kBwdThreads);
+    int cbase = 0;
+    int64_t fv[kPer];
+    load_chunk(cur, cbase, fv);
+    for (;;) {
+        if (t == 0) nlist = 0;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const bool filled = fv[q] >= 0;
+            const uint64_t bal = __ballot(filled);
+            int at = 0;
+            if (lane == 0 && bal) at = atomicAdd(&nlist, (int)__popcll(bal));
+            at = __shfl(at, 0, 64);
+            if (filled) {
+                const int e = at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                lface[e] = (int32_t)fv[q];
+                lslot[e] = (uint16_t)(cbase + q * kBwdThreads + t);
+            }
+        }
+        __syncthreads();
+        // the next chunk (of this tile or the next one) is read while this
+        // one is evaluated
+        Tile nxt = cur;
+        int nbase = cbase + kListCap;
+        bool more = true;
+        if (nbase >= tile_slots) {
+            nbase = 0;
+            more = tile_at(round + 1, nxt);
+        }
+        if (more) load_chunk(nxt, nbase, fv);
+        const int m = nlist;
+        // (a trip count uniform over the workgroup: every lane takes part
+        // in the cooperative record loads; a lane without a slot loads
+        // the list's last face, so that no one address is shared by the
+        // idle lanes of every workgroup)
+        const int32_t f_last = m > 0 ? lface[m - 1] : 0;
+        const int32_t f_idle = (f_last >= 0 && (int64_t)f_last < F) ? f_last : 0;
+        for (int e0 = 0; e0 < m; e0 += 2 * kBwdThreads) {
+            SlotIn in[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int x = e0 + t + u * kBwdThreads;
+                const int64_t f = x < m ? (int64_t)lface[x] : -1;
+                in[u].ok = f >= 0 && f < F;
+                if (recs) in[u].r = quad_load_record(recs, in[u].ok ? (int32_t)f : f_idle);
+                if (x < m) {
+                    const int sidx = lslot[x];
                     const int r = (int)__umulhi((uint32_t)sidx, m_row);
                     const int within = sidx - r * row_slots;
                     const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
-                    if (r < rows && col < cols) fv[q] = pix_to_face[tile0 + (int64_t)r * W * K + within];
+                    const int gi = cur.by * kBin + r, gj = cur.bx * kBin + col;
+                    load_slot_rest(recs, verts, faces, V, f, cur.tile0 + (int64_t)r * W * K + within,
+                                   pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
                 }
             }
 #pragma unroll
-            for (int q = 0; q < kListCap / kBwdThreads; ++q) {
-                const bool filled = fv[q] >= 0;
-                const uint64_t bal = __ballot(filled);
-                int at = 0;
-                if (lane == 0 && bal) at = atomicAdd(&nlist, (int)__popcll(bal));
-                at = __shfl(at, 0, 64);
-                if (filled) {
-                    const int e = at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
-                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-                    lface[e] = (int32_t)fv[q];
-                    lslot[e] = (uint16_t)(cbase + q * kBwdThreads + t);
-                }
-            }
-            __syncthreads();
-            const int m = nlist;
-            // (a trip count uniform over the workgroup: every lane takes part
-            // in the cooperative record loads; a lane without a slot loads
-            // the list's last face, so that no one address is shared by the
-            // idle lanes of every workgroup)
-            const int32_t f_last = m > 0 ? lface[m - 1] : 0;
-            const int32_t f_idle = (f_last >= 0 && (int64_t)f_last < F) ? f_last : 0;
-            for (int e0 = 0; e0 < m; e0 += 2 * kBwdThreads) {
-                SlotIn in[2];
-#pragma unroll
-                for (int u = 0; u < 2; ++u) {
-                    const int x = e0 + t + u * kBwdThreads;
-                    const int64_t f = x < m ? (int64_t)lface[x] : -1;
-                    in[u].ok = f >= 0 && f < F;
-                    if (recs) in[u].r = quad_load_record(recs, in[u].ok ? (int32_t)f : f_idle);
-                    if (x < m) {
-                        const int sidx = lslot[x];
-                        const int r = (int)__umulhi((uint32_t)sidx, m_row);
-                        const int within = sidx - r * row_slots;
-                        const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
-                        const int gi = by * kBin + r, gj = bx * kBin + col;
-                        load_slot_rest(recs, verts, faces, V, f, tile0 + (int64_t)r * W * K + within,
-                                       pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash);
-            }
-            __syncthreads();
+            for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash);
         }
-        for (int e = t; e < kHashSize; e += kBwdThreads) {
-            const int32_t vid = hkey[e];
-            if (vid >= 0) {
-                atomicAdd(&grad_verts[3 * (int64_t)vid + 0], from_fixed(hval[e][0]));
-                atomicAdd(&grad_verts[3 * (int64_t)vid + 1], from_fixed(hval[e][1]));
-                atomicAdd(&grad_verts[3 * (int64_t)vid + 2], from_fixed(hval[e][2]));
-            }
+        __syncthreads();
+        if (nbase == 0) {
+            // end of the tile: its sums go out, and the table is cleared
+            // for the next one
+            flush_table(hkey, hval, grad_verts, kBwdThreads);
+            if (!more) break;
+            __syncthreads();
+            clear_table(hkey, hval, kBwdThreads);
+            ++round;
         }
-        __syncthreads();   // the table is cleared for the next tile
+        cur = nxt;
+        cbase = nbase;
     }
 }
 
