@@ -333,7 +333,7 @@ dmr_status check_points(const float* points, int64_t P, const int64_t* off, int6
     if (P > (int64_t)INT32_MAX - 1) return DMR_ERROR_UNSUPPORTED;   // point ids are 32-bit inside
     int64_t pix, slots;
     if (mul_overflows(N, (int64_t)H * W, &pix) || mul_overflows(pix, K, &slots)) return DMR_ERROR_UNSUPPORTED;
-    if (slots > (int64_t)UINT32_MAX * 256) return DMR_ERROR_UNSUPPORTED;   // one backward thread per slot
+    if (slots > (int64_t)UINT32_MAX * 256) return DMR_ERROR_UNSUPPORTED;
     if (P > 0 && points == nullptr) return DMR_ERROR_INVALID_VALUE;
     if (N > 0 && off == nullptr) return DMR_ERROR_INVALID_VALUE;
     *slots_out = slots;

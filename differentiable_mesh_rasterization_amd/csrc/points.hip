@@ -332,16 +332,21 @@ hipError_t launch_points_forward(const FwdArgs& a) {
 }
 
 // ---------------------------------------------------------------------------
-// backward: one workgroup per 16x16 tile, one thread per pixel over its K
-// slots; zbuf = z_q and dists = d2 give dL/dz_q += g_z and
-// dL/d(x_q, y_q) += -2 (px - x_q, py - y_q) g_d. A point reaches the few
-// pixels within its radius, nearly all in one tile: the tile's terms are
-// summed per point in LDS (lds_accum.h), then added to grad_points with one
-// float atomic per (tile, point, coordinate).
+// backward: one workgroup per 16x16 tile; zbuf = z_q and dists = d2 give
+// dL/dz_q += g_z and dL/d(x_q, y_q) += -2 (px - x_q, py - y_q) g_d. A point
+// reaches the few pixels within its radius, nearly all in one tile: the
+// tile's terms are summed per point in LDS (lds_accum.h), then added to
+// grad_points with one float atomic per (tile, point, coordinate).
+// The tile's slots are read slot-linearly in chunks of kPointList
+// (coalesced, the next chunk issued before the current one is evaluated);
+// the filled ones (about one in ten) are compacted into an LDS list, and
+// each thread evaluates the list's slots two at a time.
 // ---------------------------------------------------------------------------
 // The table size of the mesh backward (1024 entries); a 512-entry table,
 // with more resident workgroups, measured 14% slower.
 constexpr int kPointHashBits = kHashBits;
+constexpr int kPointList = 1536;
+static_assert(kPointList % kPointThreads == 0, "whole loads per thread");
 
 __global__ void point_zero(float* p, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -357,44 +362,94 @@ __global__ __launch_bounds__(kPointThreads) void point_backward(const float* __r
                                                                 float* __restrict__ grad) {
     __shared__ int32_t hkey[1 << kPointHashBits];
     __shared__ unsigned long long hval[1 << kPointHashBits][3];
-    clear_table<kPointHashBits>(hkey, hval, kPointThreads);
-    __syncthreads();
+    __shared__ int32_t lpt[kPointList];
+    __shared__ uint16_t lslot[kPointList];   // slot index within the tile
+    __shared__ int32_t nlist;
+    constexpr int kPer = kPointList / kPointThreads;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
     const int64_t per_img = (int64_t)nbx * nby;
     const int64_t b = blockIdx.x;
     const int64_t n = b / per_img;
     const int rem = (int)(b - n * per_img);
     const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
-    const int i = by * kBin + (int)threadIdx.x / kBin, j = bx * kBin + (int)threadIdx.x % kBin;
-    if (i < H && j < W) {
-        const float px = pixel_centre(j, W), py = pixel_centre(i, H);
-        const int64_t s0 = (((int64_t)n * H + i) * W + j) * K;
-        // kBwdChunk slots at a time: all their loads are issued before any
-        // is used, so a pixel's slots cost one round of memory latency per
-        // chunk rather than one per slot
-        constexpr int kBwdChunk = 8;
-        for (int k0 = 0; k0 < K; k0 += kBwdChunk) {
-            int64_t q[kBwdChunk];
+    const int rows = min(kBin, H - by * kBin), cols = min(kBin, W - bx * kBin);
+    const int64_t tile0 = (((int64_t)n * H + by * kBin) * W + bx * kBin) * K;
+    // tile slot s -> (row, slot within the row, column): divisions by
+    // multiplication (exact while s * divisor < 2^32)
+    const int row_slots = kBin * K;
+    const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
+    const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
+    const int tile_slots = kBin * row_slots;
+    auto load_chunk = [&](int cbase, int64_t (&fv)[kPer]) {
 #pragma unroll
-            for (int c = 0; c < kBwdChunk; ++c) q[c] = k0 + c < K ? idx[s0 + k0 + c] : -1;
-            float g_z[kBwdChunk], g_d[kBwdChunk], x[kBwdChunk], y[kBwdChunk];
-#pragma unroll
-            for (int c = 0; c < kBwdChunk; ++c) {
-                const bool ok = q[c] >= 0 && q[c] < P;
-                g_z[c] = ok && gz ? gz[s0 + k0 + c] : 0.0f;
-                g_d[c] = ok && gd ? gd[s0 + k0 + c] : 0.0f;
-                x[c] = ok ? pts[3 * q[c]] : 0.0f;
-                y[c] = ok ? pts[3 * q[c] + 1] : 0.0f;
-            }
-#pragma unroll
-            for (int c = 0; c < kBwdChunk; ++c) {
-                if (q[c] < 0 || q[c] >= P) continue;
-                const float gx = -2.0f * (px - x[c]) * g_d[c];
-                const float gy = -2.0f * (py - y[c]) * g_d[c];
-                vertex_add<kPointHashBits>(hkey, hval, grad, q[c], gx, gy, g_z[c], true);
+        for (int q = 0; q < kPer; ++q) {
+            const int sidx = cbase + q * kPointThreads + t;
+            fv[q] = -1;
+            if (sidx < tile_slots) {
+                const int r = (int)__umulhi((uint32_t)sidx, m_row);
+                const int within = sidx - r * row_slots;
+                const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
+                if (r < rows && col < cols) fv[q] = idx[tile0 + (int64_t)r * W * K + within];
             }
         }
+    };
+    clear_table<kPointHashBits>(hkey, hval, kPointThreads);
+    int64_t fv[kPer];
+    load_chunk(0, fv);
+    for (int cbase = 0; cbase < tile_slots; cbase += kPointList) {
+        if (t == 0) nlist = 0;
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kPer; ++q) {
+            const bool filled = fv[q] >= 0 && fv[q] < P;
+            const uint64_t bal = __ballot(filled);
+            int at = 0;
+            if (lane == 0 && bal) at = atomicAdd(&nlist, (int)__popcll(bal));
+            at = __shfl(at, 0, 64);
+            if (filled) {
+                const int e = at + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32),
+                                                                  __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                lpt[e] = (int32_t)fv[q];
+                lslot[e] = (uint16_t)(cbase + q * kPointThreads + t);
+            }
+        }
+        __syncthreads();
+        if (cbase + kPointList < tile_slots) load_chunk(cbase + kPointList, fv);
+        const int m = nlist;
+        for (int e0 = 0; e0 < m; e0 += 2 * kPointThreads) {
+            int32_t pq[2];
+            float px[2], py[2], g_z[2], g_d[2], x[2], y[2];
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const int e = e0 + t + u * kPointThreads;
+                pq[u] = -1;
+                px[u] = py[u] = g_z[u] = g_d[u] = x[u] = y[u] = 0.0f;
+                if (e < m) {
+                    pq[u] = lpt[e];
+                    const int sidx = lslot[e];
+                    const int r = (int)__umulhi((uint32_t)sidx, m_row);
+                    const int within = sidx - r * row_slots;
+                    const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
+                    const int64_t so = tile0 + (int64_t)r * W * K + within;
+                    px[u] = pixel_centre(bx * kBin + col, W);
+                    py[u] = pixel_centre(by * kBin + r, H);
+                    g_z[u] = gz ? gz[so] : 0.0f;
+                    g_d[u] = gd ? gd[so] : 0.0f;
+                    x[u] = pts[3 * (int64_t)pq[u]];
+                    y[u] = pts[3 * (int64_t)pq[u] + 1];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                if (pq[u] < 0) continue;
+                const float gx = -2.0f * (px[u] - x[u]) * g_d[u];
+                const float gy = -2.0f * (py[u] - y[u]) * g_d[u];
+                vertex_add<kPointHashBits>(hkey, hval, grad, pq[u], gx, gy, g_z[u], true);
+            }
+        }
+        __syncthreads();
     }
-    __syncthreads();
     flush_table<kPointHashBits>(hkey, hval, grad, kPointThreads);
 }
 
