@@ -267,11 +267,10 @@ __device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsi
     vertex_add3(hkey, hval, grad_verts, in.vi, g, use_hash);
 }
 
-// Tiles come from the grid (one workgroup per tile) or, with the forward's
-// workspace, from its heaviest-first bin order, dealt to the resident
-// workgroups in snake order (round r gives workgroup w the tile r*G + w, or
-// r*G + G-1-w for odd r) until a bin without faces (those come last and have
-// no filled slot) or the end of the order. SETTINGS holds the
+// One workgroup per tile: workgroup w takes bin w or, with the forward's
+// workspace, the w-th bin of its heaviest-first order (so that the longest
+// tiles start first and the dispatcher fills in behind them); a bin without
+// faces has no filled slot and ends at once. SETTINGS holds the
 // DMR_RASTER_* bits that change the per-slot evaluation (perspective
 // correction, unclipped barycentrics), fixed at compile time so that each
 // variant carries only its own arithmetic.
@@ -279,14 +278,14 @@ __device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsi
 // A tile's slots are read slot-linearly in chunks of kListCap (coalesced,
 // all loads of a chunk in flight together, and the next chunk's issued
 // before this one is evaluated); the filled ones are compacted into an LDS
-// list (their order is free: the LDS sums are exact), and each
-// thread evaluates the list's slots two at a time, the second slot's loads
+// list (their order is free: the LDS sums are exact), and each thread
+// evaluates the list's slots two at a time, the second slot's loads
 // issued with the first's. The face records are loaded a lane quad at a
 // time (quad_load_record).
 template <uint32_t SETTINGS>
 __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const FaceRec* __restrict__ recs, const int32_t* __restrict__ bin_order, const int32_t* __restrict__ bin_count,
-    int64_t bins, const float* __restrict__ verts, const int64_t* __restrict__ faces, int64_t V, int64_t F,
+    const float* __restrict__ verts, const int64_t* __restrict__ faces, int64_t V, int64_t F,
     int32_t H, int32_t W, int32_t K, int32_t nbx, int32_t nby, const int64_t* __restrict__ pix_to_face,
     const float* __restrict__ gzb, const float* __restrict__ gba, const float* __restrict__ gds,
     float* __restrict__ grad_verts, int32_t use_hash_arg) {
@@ -299,38 +298,25 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const int64_t per_img = (int64_t)nbx * nby;
     const int t = threadIdx.x;
     const int lane = t & 63;
-    const int64_t G = gridDim.x;
     // tile slot s -> (row, slot within the row, column): divisions by
     // multiplication (exact while s * divisor < 2^32)
     const int row_slots = kBin * K;
     const uint32_t m_row = 0xffffffffu / (uint32_t)row_slots + 1u;
     const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
     const int tile_slots = kBin * row_slots;
-    // tile of round r (false past the last one)
-    struct Tile {
-        int64_t tile0;
-        int by, bx, rows, cols;
-    };
-    auto tile_at = [&](int64_t r, Tile& T) -> bool {
-        const int64_t idx = r * G + ((r & 1) ? G - 1 - blockIdx.x : blockIdx.x);
-        if (idx >= bins) return false;
-        int64_t b = idx;
-        if (bin_order) {
-            b = bin_order[idx];
-            if (bin_count[b] == 0) return false;
-        }
-        const int64_t n = b / per_img;
-        const int rem = (int)(b - n * per_img);
-        T.by = rem / nbx;
-        T.bx = rem - T.by * nbx;
-        T.rows = min(kBin, H - T.by * kBin);
-        T.cols = min(kBin, W - T.bx * kBin);
-        T.tile0 = (((int64_t)n * H + T.by * kBin) * W + T.bx * kBin) * K;
-        return true;
-    };
+    int64_t b = blockIdx.x;
+    if (bin_order) {
+        b = bin_order[b];
+        if (bin_count[b] == 0) return;   // no face, no filled slot
+    }
+    const int64_t n = b / per_img;
+    const int rem = (int)(b - n * per_img);
+    const int by = rem / nbx, bx = rem - (rem / nbx) * nbx;
+    const int rows = min(kBin, H - by * kBin), cols = min(kBin, W - bx * kBin);
+    const int64_t tile0 = (((int64_t)n * H + by * kBin) * W + bx * kBin) * K;
     constexpr int kPer = kListCap / kBwdThreads;
     // the chunk's face ids (-1 outside the image or past the tile)
-    auto load_chunk = [&](const Tile& T, int cbase, int64_t (&fv)[kPer]) {
+    auto load_chunk = [&](int cbase, int64_t (&fv)[kPer]) {
 #pragma unroll
         for (int q = 0; q < kPer; ++q) {
             const int sidx = cbase + q * kBwdThreads + t;
@@ -339,18 +325,14 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
                 const int r = (int)__umulhi((uint32_t)sidx, m_row);
                 const int within = sidx - r * row_slots;
                 const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
-                if (r < T.rows && col < T.cols) fv[q] = pix_to_face[T.tile0 + (int64_t)r * W * K + within];
+                if (r < rows && col < cols) fv[q] = pix_to_face[tile0 + (int64_t)r * W * K + within];
             }
         }
     };
-    Tile cur;
-    int64_t round = 0;
-    if (!tile_at(round, cur)) return;
     clear_table(hkey, hval, kBwdThreads);
-    int cbase = 0;
     int64_t fv[kPer];
-    load_chunk(cur, cbase, fv);
-    for (;;) {
+    load_chunk(0, fv);
+    for (int cbase = 0; cbase < tile_slots; cbase += kListCap) {
         if (t == 0) nlist = 0;
         __syncthreads();
 #pragma unroll
@@ -368,16 +350,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
             }
         }
         __syncthreads();
-        // the next chunk (of this tile or the next one) is read while this
-        // one is evaluated
-        Tile nxt = cur;
-        int nbase = cbase + kListCap;
-        bool more = true;
-        if (nbase >= tile_slots) {
-            nbase = 0;
-            more = tile_at(round + 1, nxt);
-        }
-        if (more) load_chunk(nxt, nbase, fv);
+        // the next chunk is read while this one is evaluated
+        if (cbase + kListCap < tile_slots) load_chunk(cbase + kListCap, fv);
         const int m = nlist;
         // (a trip count uniform over the workgroup: every lane takes part
         // in the cooperative record loads; a lane without a slot loads
@@ -398,8 +372,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
                     const int r = (int)__umulhi((uint32_t)sidx, m_row);
                     const int within = sidx - r * row_slots;
                     const int col = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
-                    const int gi = cur.by * kBin + r, gj = cur.bx * kBin + col;
-                    load_slot_rest(recs, verts, faces, V, f, cur.tile0 + (int64_t)r * W * K + within,
+                    const int gi = by * kBin + r, gj = bx * kBin + col;
+                    load_slot_rest(recs, verts, faces, V, f, tile0 + (int64_t)r * W * K + within,
                                    pixel_centre(gj, W), pixel_centre(gi, H), gzb, gba, gds, in[u]);
                 }
             }
@@ -407,41 +381,16 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
             for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash);
         }
         __syncthreads();
-        if (nbase == 0) {
-            // end of the tile: its sums go out, and the table is cleared
-            // for the next one
-            flush_table(hkey, hval, grad_verts, kBwdThreads);
-            if (!more) break;
-            __syncthreads();
-            clear_table(hkey, hval, kBwdThreads);
-            ++round;
-        }
-        cur = nxt;
-        cbase = nbase;
     }
+    flush_table(hkey, hval, grad_verts, kBwdThreads);
 }
 
 template <uint32_t SETTINGS>
-static void launch_backward_slots(const BwdArgs& a, bool reuse, const FaceRec* recs, const int32_t* order,
+static void launch_backward_slots(const BwdArgs& a, const FaceRec* recs, const int32_t* order,
                                   const int32_t* count) {
-    int64_t grid = a.L.bins;
-    if (reuse) {
-        // as many workgroups as stay resident; each takes its share of the order
-        static int resident_per_cu = 0;
-        int dev = 0, cus = 0;
-        if (resident_per_cu == 0 &&
-            hipOccupancyMaxActiveBlocksPerMultiprocessor(&resident_per_cu, backward_slots<SETTINGS>, kBwdThreads,
-                                                         0) != hipSuccess)
-            resident_per_cu = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            cus = 0;
-        const int64_t resident = (int64_t)std::max(1, cus) * std::max(1, resident_per_cu);
-        grid = std::min<int64_t>(grid, resident);
-    }
-    backward_slots<SETTINGS><<<(unsigned)grid, kBwdThreads, 0, a.stream>>>(
-        recs, order, count, a.L.bins, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx,
-        (int32_t)a.L.nby, a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
+    backward_slots<SETTINGS><<<(unsigned)a.L.bins, kBwdThreads, 0, a.stream>>>(
+        recs, order, count, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx, (int32_t)a.L.nby,
+        a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
 }
 
 hipError_t launch_backward(const BwdArgs& a) {
@@ -450,8 +399,7 @@ hipError_t launch_backward(const BwdArgs& a) {
     const bool work = npix > 0 && a.F > 0;
     // With the forward's workspace, its per-face records (vertex positions,
     // 1/A, inverse edge lengths) replace the per-slot gathers and divisions,
-    // and its heaviest-first bin order and counts deal the non-empty tiles
-    // to the resident workgroups.
+    // and its heaviest-first bin order and counts order the tiles.
     const bool reuse = a.reuse_forward && work;
     if (n3 > 0) {
         timing_begin(kKZeroGrad, a.stream);
@@ -465,10 +413,10 @@ hipError_t launch_backward(const BwdArgs& a) {
     constexpr uint32_t kP = DMR_RASTER_PERSPECTIVE_CORRECT, kU = DMR_RASTER_UNCLIPPED_BARY;
     timing_begin(kKBackward, a.stream);
     switch (a.settings & (kP | kU)) {
-        case 0: launch_backward_slots<0>(a, reuse, recs, order, count); break;
-        case kP: launch_backward_slots<kP>(a, reuse, recs, order, count); break;
-        case kU: launch_backward_slots<kU>(a, reuse, recs, order, count); break;
-        default: launch_backward_slots<kP | kU>(a, reuse, recs, order, count); break;
+        case 0: launch_backward_slots<0>(a, recs, order, count); break;
+        case kP: launch_backward_slots<kP>(a, recs, order, count); break;
+        case kU: launch_backward_slots<kU>(a, recs, order, count); break;
+        default: launch_backward_slots<kP | kU>(a, recs, order, count); break;
     }
     timing_end(kKBackward, a.stream);
     return hipGetLastError();
