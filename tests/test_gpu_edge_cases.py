@@ -4,9 +4,9 @@ pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
 thousands of faces in one bin, heavy bins split into quarter items, hundreds
 of faces each covering every pixel (whole and split bins), subnormal depths,
-faces
-using another mesh's vertices, the largest image side, hundreds of small
-meshes, invalid vertex indices, and the hand-worked cases."""
+faces using another mesh's vertices, the largest image side, hundreds of
+small meshes, invalid vertex indices, and the hand-worked cases; every case
+also through the backward pass."""
 
 import json
 import os
@@ -15,8 +15,8 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import GpuCase, host, require_gpu, say
-from parity import assert_forward_parity, compare_forward, oracle_excuse
+from gpu_util import GpuCase, host, require_gpu, say, to_dev
+from parity import assert_forward_parity, compare_forward, oracle_excuse, rel_l2
 
 pytestmark = pytest.mark.gpu
 
@@ -256,6 +256,34 @@ def many_small_meshes():
 def test_edge_case(dmr, name):
     say(f"[gpu] edge case {name}")
     _check(*CASES[name]())
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_edge_case_backward(dmr, name):
+    # the same inputs through the backward pass, with seeded N(0, 1) upstream
+    # gradients on every slot (the padding's must be ignored by both sides)
+    verts, faces, offsets, H, W, K, blur = CASES[name]()
+    verts = np.asarray(verts, np.float32).reshape(-1, 3)
+    faces = np.asarray(faces, np.int64).reshape(-1, 3)
+    offsets = np.asarray(offsets, np.int64)
+    say(f"[gpu] edge case backward {name}")
+    g = GpuCase(verts, faces, offsets, H, W, K, blur)
+    p2f = g.forward()[0]
+    ref_p2f = oracle.rasterize(verts, faces, offsets, H, W, K, blur)[0]
+    assert np.array_equal(p2f.cpu().numpy(), ref_p2f)
+    rng = np.random.Generator(np.random.PCG64(7000 + list(CASES).index(name)))
+    shape = ref_p2f.shape
+    gz = rng.standard_normal(shape).astype(np.float32)
+    gb = rng.standard_normal(shape + (3,)).astype(np.float32)
+    gd = rng.standard_normal(shape).astype(np.float32)
+    gv = g.backward(p2f, to_dev(gz), to_dev(gb), to_dev(gd)).cpu().numpy()
+    ref = oracle.backward(verts, faces, offsets, H, W, K, blur, ref_p2f, gz, gb, gd)
+    if not np.any(ref_p2f >= 0):
+        assert not np.any(gv)
+    else:
+        err = rel_l2(gv, ref)
+        say(f"  rel L2 = {err:.2e}  |ref| = {np.linalg.norm(ref):.3e}")
+        assert err <= 1e-4
 
 
 def test_invalid_vertex_index_is_flagged(dmr):
