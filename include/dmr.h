@@ -153,10 +153,8 @@ dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t*
  *              faces, and its bin order and counts schedule the tiles (bins
  *              without faces are skipped). The caller guarantees this; it is
  *              not checked, and any other content gives wrong gradients. The
- *              call writes one counter word of the workspace header (its tile
- *              queue), so backward calls sharing a workspace must not overlap
- *              in time. Without that bit the workspace is not used and may be
- *              NULL.
+ *              call only reads the workspace. Without that bit the workspace
+ *              is not used and may be NULL.
  * Contributions are summed per 16x16 tile and vertex in LDS, then added to
  * grad_verts with float32 atomics, so the rounding of grad_verts may differ
  * between runs.
