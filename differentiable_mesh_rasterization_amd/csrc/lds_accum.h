@@ -1,7 +1,13 @@
-// Per-workgroup LDS accumulation of float triples keyed by a 32-bit id
-// (a vertex or a point), for gradients that many lanes of a workgroup add
-// to the same few ids: an open-addressing table of 64-bit fixed-point sums,
-// flushed with one float atomic per (id, coordinate).
+// Per-workgroup LDS accumulation of float triples keyed by an id (a vertex or
+// a point), for gradients that many lanes of a workgroup add to the same few
+// ids: an open-addressing table of 64-bit fixed-point sums, flushed with one
+// float atomic per (id, coordinate).
+//
+// Each entry's fixed-point scale is relative, not absolute: it is set by the
+// first contribution that inserts the entry (the power of two just above the
+// largest magnitude of its three coordinates) and stored in the key word next
+// to the id, so the accuracy of the sums does not depend on the scale of the
+// upstream gradients.
 #pragma once
 
 #include "dmr_internal.h"
@@ -12,126 +18,175 @@ constexpr int kHashBits = 10;
 constexpr int kHashSize = 1 << kHashBits;
 constexpr int kProbe = 32;
 
-// LDS sums are kept in 64-bit fixed point with kFixBits fractional bits: an
-// integer LDS atomic add is about 20x faster than a float one on gfx950 and
-// serialises conflicting lanes without retry loops. A contribution is
-// rounded to a multiple of 2^-kFixBits (3.7e-9); only contributions below
-// kFixLimit in magnitude take this path (larger ones go straight to global
-// float atomics), so a tile's sum for one vertex coordinate -- at most
-// 256 pixels x 64 slots contributions -- stays below 2^34 < 2^(63-kFixBits).
-constexpr int kFixBits = 28;
-constexpr float kFixLimit = 0x1.0p20f;
+// Key word of an entry: the id in the low kIdBits bits, the entry's exponent
+// code (below) in the high 8 bits; all ones marks an empty entry. Ids up to
+// kTableMaxId can use the table (larger ones would collide with the empty
+// mark or overflow the id field); callers with larger ids pass use_hash =
+// false and add every contribution with global float atomics.
+constexpr int kIdBits = 24;
+constexpr uint32_t kIdMask = (1u << kIdBits) - 1u;
+constexpr uint32_t kEmptyKey = 0xffffffffu;
+constexpr int64_t kTableMaxId = (int64_t)kIdMask - 1;
 
-// (double)v * 2^kFixBits is exact; adding 1.5 * 2^52 rounds it to the
-// nearest integer (ties to even), which then sits in the low mantissa bits
-// of the sum as a two's complement offset from those of 1.5 * 2^52 (valid
-// for magnitudes below 2^51, here below 2^48).
-__device__ __forceinline__ unsigned long long to_fixed(float v) {
+// Fixed point relative to an entry exponent e (every coordinate of the
+// entry's first contribution is below 2^e in magnitude): a contribution is
+// rounded to a multiple of 2^(e - kFixFrac) and taken into the entry only if
+// its coordinates are below 2^(e + kFixAhead); larger ones go straight to
+// global float atomics. A tile adds at most 2^14 contributions to one entry
+// (256 pixels x 64 slots), so a sum stays below 2^(14 + kFixAhead +
+// kFixFrac) = 2^62 units. The quantum is 2^-34 relative to the first
+// contribution, far below binary32 resolution.
+constexpr int kFixFrac = 34;
+constexpr int kFixAhead = 14;
+static_assert(14 + kFixFrac + kFixAhead <= 62, "64-bit fixed-point headroom");
+
+// Exponent code of a magnitude m (finite, > 0): the biased binary32 exponent
+// of m, at least 1, so that m < 2^(code - 126). 0 marks "no contribution"
+// (m == 0), 255 "not finite".
+__device__ __forceinline__ uint32_t mag_code(float m) {
+    const uint32_t eb = __float_as_uint(m) >> 23;   // m >= 0: the sign bit is clear
+    return m == 0.0f ? 0u : (eb == 0u ? 1u : eb);
+}
+
+// 2^k as a binary64 for |k| well inside the normal range.
+__device__ __forceinline__ double pow2d(int k) {
+    return __longlong_as_double((long long)(1023 + k) << 52);
+}
+
+// v / 2^(e - kFixFrac) rounded to the nearest integer, as a two's complement
+// 64-bit pattern. For an entry with code c, e = c - 126. The product is
+// exact in binary64 (a power-of-two scale); adding 1.5 * 2^52 rounds it to
+// the nearest integer (ties to even), which then sits in the low mantissa
+// bits of the sum as an offset from those of 1.5 * 2^52 (valid for
+// magnitudes below 2^51; here below 2^(kFixAhead + kFixFrac) = 2^48).
+__device__ __forceinline__ unsigned long long to_fixed(float v, uint32_t code) {
     const double kRound = 6755399441055744.0;   // 1.5 * 2^52
-    const double d = (double)v * (double)(1ull << kFixBits) + kRound;
+    const double d = (double)v * pow2d(kFixFrac + 126 - (int)code) + kRound;
     return (unsigned long long)(__double_as_longlong(d) - __double_as_longlong(kRound));
 }
-__device__ __forceinline__ float from_fixed(unsigned long long x) {
-    return (float)((double)(long long)x * (1.0 / (double)(1ull << kFixBits)));
+__device__ __forceinline__ float from_fixed(unsigned long long x, uint32_t code) {
+    return (float)((double)(long long)x * pow2d((int)code - 126 - kFixFrac));
+}
+
+// Finds or inserts the entry of `id` for a contribution of exponent code
+// `code` (1..254); returns its slot and the entry's code, or -1 when the
+// probe sequence finds no room. `first` is the result of the first probe's
+// compare-and-swap at slot h0 (issued by the caller).
+template <int HB>
+__device__ __forceinline__ int table_find(uint32_t* hkey, uint32_t id, uint32_t code, uint32_t h0, uint32_t first,
+                                          uint32_t& entry_code) {
+    uint32_t cur = first;
+    uint32_t h = h0;
+#pragma unroll 1
+    for (int p = 0;; ) {
+        if (cur == kEmptyKey) {
+            entry_code = code;
+            return (int)h;
+        }
+        if ((cur & kIdMask) == id) {
+            entry_code = cur >> kIdBits;
+            return (int)h;
+        }
+        if (++p >= kProbe) return -1;
+        h = (h + 1) & ((1u << HB) - 1u);
+        cur = atomicCAS(&hkey[h], kEmptyKey, id | (code << kIdBits));
+    }
+}
+
+__device__ __forceinline__ uint32_t hash_slot0(uint32_t id, int hb) { return (id * 2654435761u) >> (32 - hb); }
+
+__device__ __forceinline__ void global_add3(float* __restrict__ grad, int64_t vi, float gx, float gy, float gz) {
+    atomicAdd(&grad[3 * vi + 0], gx);
+    atomicAdd(&grad[3 * vi + 1], gy);
+    atomicAdd(&grad[3 * vi + 2], gz);
 }
 
 // Adds one id's three partials into the tile's LDS hash table (2^HB
-// entries), or into grad_verts directly when the table has no room for it
-// or a value is too large for the fixed-point sums.
+// entries), or into grad directly when the table cannot take them (no room,
+// a coordinate not finite, or too large for the entry's scale). A
+// contribution of three zeros adds nothing.
 template <int HB = kHashBits>
-__device__ __forceinline__ void vertex_add(int32_t* hkey, unsigned long long (*hval)[3],
-                                           float* __restrict__ grad_verts, int64_t vi, float gx, float gy, float gz,
+__device__ __forceinline__ void vertex_add(uint32_t* hkey, unsigned long long (*hval)[3],
+                                           float* __restrict__ grad, int64_t vi, float gx, float gy, float gz,
                                            bool use_hash) {
-    const float lim = kFixLimit;
-    if (use_hash && fabsf(gx) < lim && fabsf(gy) < lim && fabsf(gz) < lim) {
-        const int32_t vid = (int32_t)vi;
-        uint32_t h = ((uint32_t)vid * 2654435761u) >> (32 - HB);
-#pragma unroll 1
-        for (int p = 0; p < kProbe; ++p) {
-            const int32_t cur = atomicCAS(&hkey[h], -1, vid);
-            if (cur == -1 || cur == vid) {
-                atomicAdd(&hval[h][0], to_fixed(gx));
-                atomicAdd(&hval[h][1], to_fixed(gy));
-                atomicAdd(&hval[h][2], to_fixed(gz));
-                return;
-            }
-            h = (h + 1) & ((1u << HB) - 1u);
+    const float m = fmaxf(fabsf(gx), fmaxf(fabsf(gy), fabsf(gz)));   // fmaxf drops a NaN operand
+    const uint32_t code = mag_code(m);
+    const bool nan = (gx != gx) || (gy != gy) || (gz != gz);
+    if (code == 0u && !nan) return;   // three zeros: nothing to add
+    if (use_hash && m <= 3.402823466e38f && !nan) {
+        const uint32_t id = (uint32_t)vi;
+        const uint32_t h = hash_slot0(id, HB);
+        const uint32_t first = atomicCAS(&hkey[h], kEmptyKey, id | (code << kIdBits));
+        uint32_t ec = 0;
+        const int slot = table_find<HB>(hkey, id, code, h, first, ec);
+        if (slot >= 0 && code <= ec + kFixAhead) {
+            atomicAdd(&hval[slot][0], to_fixed(gx, ec));
+            atomicAdd(&hval[slot][1], to_fixed(gy, ec));
+            atomicAdd(&hval[slot][2], to_fixed(gz, ec));
+            return;
         }
     }
-    atomicAdd(&grad_verts[3 * vi + 0], gx);
-    atomicAdd(&grad_verts[3 * vi + 1], gy);
-    atomicAdd(&grad_verts[3 * vi + 2], gz);
+    global_add3(grad, vi, gx, gy, gz);
 }
-
 
 // The three vertices of one face at once: the first probe of all three is
 // issued before any result is waited for, further probes (rare) follow in a
 // loop, then the nine fixed-point adds (or global float atomics for a
 // vertex the table cannot take).
 template <int HB = kHashBits>
-__device__ __forceinline__ void vertex_add3(int32_t* hkey, unsigned long long (*hval)[3],
+__device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (*hval)[3],
                                             float* __restrict__ grad_verts, const int64_t (&vi)[3],
                                             const float (&g)[9], bool use_hash) {
-    const float lim = kFixLimit;
-    bool elig[3];
-    uint32_t h[3];
-    int32_t cur[3];
+    uint32_t code[3], h[3], cur[3];
+    bool elig[3], zero[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        elig[k] = use_hash && fabsf(g[3 * k]) < lim && fabsf(g[3 * k + 1]) < lim && fabsf(g[3 * k + 2]) < lim;
-        h[k] = ((uint32_t)(int32_t)vi[k] * 2654435761u) >> (32 - HB);
-        cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], -1, (int32_t)vi[k]) : 0;
+        const float gx = g[3 * k], gy = g[3 * k + 1], gz = g[3 * k + 2];
+        const float m = fmaxf(fabsf(gx), fmaxf(fabsf(gy), fabsf(gz)));   // fmaxf drops a NaN operand
+        const bool nan = (gx != gx) || (gy != gy) || (gz != gz);
+        code[k] = mag_code(m);
+        zero[k] = code[k] == 0u && !nan;   // three zeros: nothing to add
+        elig[k] = use_hash && !zero[k] && m <= 3.402823466e38f && !nan;
+        const uint32_t id = (uint32_t)vi[k];
+        h[k] = hash_slot0(id, HB);
+        cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], kEmptyKey, id | (code[k] << kIdBits)) : 0u;
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
-        const int32_t vid = (int32_t)vi[k];
+        if (zero[k]) continue;
         int slot = -1;
-        if (elig[k]) {
-            if (cur[k] == -1 || cur[k] == vid) {
-                slot = (int)h[k];
-            } else {
-                uint32_t hp = h[k];
-#pragma unroll 1
-                for (int p = 1; p < kProbe; ++p) {
-                    hp = (hp + 1) & ((1u << HB) - 1u);
-                    const int32_t c = atomicCAS(&hkey[hp], -1, vid);
-                    if (c == -1 || c == vid) {
-                        slot = (int)hp;
-                        break;
-                    }
-                }
-            }
-        }
-        if (slot >= 0) {
-            atomicAdd(&hval[slot][0], to_fixed(g[3 * k]));
-            atomicAdd(&hval[slot][1], to_fixed(g[3 * k + 1]));
-            atomicAdd(&hval[slot][2], to_fixed(g[3 * k + 2]));
+        uint32_t ec = 0;
+        if (elig[k]) slot = table_find<HB>(hkey, (uint32_t)vi[k], code[k], h[k], cur[k], ec);
+        if (slot >= 0 && code[k] <= ec + kFixAhead) {
+            atomicAdd(&hval[slot][0], to_fixed(g[3 * k], ec));
+            atomicAdd(&hval[slot][1], to_fixed(g[3 * k + 1], ec));
+            atomicAdd(&hval[slot][2], to_fixed(g[3 * k + 2], ec));
         } else {
-            atomicAdd(&grad_verts[3 * vi[k] + 0], g[3 * k]);
-            atomicAdd(&grad_verts[3 * vi[k] + 1], g[3 * k + 1]);
-            atomicAdd(&grad_verts[3 * vi[k] + 2], g[3 * k + 2]);
+            global_add3(grad_verts, vi[k], g[3 * k], g[3 * k + 1], g[3 * k + 2]);
         }
     }
 }
 
 // Flushes a workgroup's table into grad (3 floats per id) with float atomics.
 template <int HB = kHashBits>
-__device__ __forceinline__ void flush_table(const int32_t* hkey, const unsigned long long (*hval)[3],
+__device__ __forceinline__ void flush_table(const uint32_t* hkey, const unsigned long long (*hval)[3],
                                             float* __restrict__ grad, int nthreads) {
     for (int e = threadIdx.x; e < (1 << HB); e += nthreads) {
-        const int32_t vid = hkey[e];
-        if (vid >= 0) {
-            atomicAdd(&grad[3 * (int64_t)vid + 0], from_fixed(hval[e][0]));
-            atomicAdd(&grad[3 * (int64_t)vid + 1], from_fixed(hval[e][1]));
-            atomicAdd(&grad[3 * (int64_t)vid + 2], from_fixed(hval[e][2]));
+        const uint32_t key = hkey[e];
+        if (key != kEmptyKey) {
+            const int64_t vid = (int64_t)(key & kIdMask);
+            const uint32_t ec = key >> kIdBits;
+            atomicAdd(&grad[3 * vid + 0], from_fixed(hval[e][0], ec));
+            atomicAdd(&grad[3 * vid + 1], from_fixed(hval[e][1], ec));
+            atomicAdd(&grad[3 * vid + 2], from_fixed(hval[e][2], ec));
         }
     }
 }
 
 template <int HB = kHashBits>
-__device__ __forceinline__ void clear_table(int32_t* hkey, unsigned long long (*hval)[3], int nthreads) {
+__device__ __forceinline__ void clear_table(uint32_t* hkey, unsigned long long (*hval)[3], int nthreads) {
     for (int e = threadIdx.x; e < (1 << HB); e += nthreads) {
-        hkey[e] = -1;
+        hkey[e] = kEmptyKey;
         hval[e][0] = 0;
         hval[e][1] = 0;
         hval[e][2] = 0;

@@ -359,8 +359,8 @@ __global__ __launch_bounds__(kPointThreads) void point_backward(const float* __r
                                                                 int32_t nby, const int64_t* __restrict__ idx,
                                                                 const float* __restrict__ gz,
                                                                 const float* __restrict__ gd,
-                                                                float* __restrict__ grad) {
-    __shared__ int32_t hkey[1 << kPointHashBits];
+                                                                float* __restrict__ grad, int32_t use_hash) {
+    __shared__ uint32_t hkey[1 << kPointHashBits];
     __shared__ unsigned long long hval[1 << kPointHashBits][3];
     __shared__ int32_t lpt[kPointList];
     __shared__ uint16_t lslot[kPointList];   // slot index within the tile
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kPointThreads) void point_backward(const float* __r
                 if (pq[u] < 0) continue;
                 const float gx = -2.0f * (px[u] - x[u]) * g_d[u];
                 const float gy = -2.0f * (py[u] - y[u]) * g_d[u];
-                vertex_add<kPointHashBits>(hkey, hval, grad, pq[u], gx, gy, g_z[u], true);
+                vertex_add<kPointHashBits>(hkey, hval, grad, pq[u], gx, gy, g_z[u], use_hash != 0);
             }
         }
         __syncthreads();
@@ -462,7 +462,8 @@ hipError_t launch_points_backward(const PointBwdArgs& a) {
     const int64_t bins = a.N * (int64_t)nbx * nby;
     if (bins > 0 && a.P > 0 && (a.gz || a.gd))
         point_backward<<<(unsigned)bins, kPointThreads, 0, a.stream>>>(a.points, a.P, a.H, a.W, a.K, nbx, nby,
-                                                                        a.idx, a.gz, a.gd, a.grad_points);
+                                                                        a.idx, a.gz, a.gd, a.grad_points,
+                                                                        a.P - 1 <= kTableMaxId ? 1 : 0);
     timing_end(kKPointBwd, a.stream);
     return hipGetLastError();
 }

@@ -257,7 +257,7 @@ __device__ __forceinline__ void load_slot_rest(const FaceRec* __restrict__ recs,
 }
 
 template <uint32_t SETTINGS>
-__device__ __forceinline__ void apply_slot(const SlotIn& in, int32_t* hkey, unsigned long long (*hval)[3],
+__device__ __forceinline__ void apply_slot(const SlotIn& in, uint32_t* hkey, unsigned long long (*hval)[3],
                                            float* __restrict__ grad_verts, bool use_hash) {
     if (!in.ok) return;
     PairState st;
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     int32_t H, int32_t W, int32_t K, int32_t nbx, int32_t nby, const int64_t* __restrict__ pix_to_face,
     const float* __restrict__ gzb, const float* __restrict__ gba, const float* __restrict__ gds,
     float* __restrict__ grad_verts, int32_t use_hash_arg) {
-    __shared__ int32_t hkey[kHashSize];
+    __shared__ uint32_t hkey[kHashSize];
     __shared__ unsigned long long hval[kHashSize][3];
     __shared__ int32_t lface[kListCap];
     __shared__ uint16_t lslot[kListCap];   // slot index within the tile
@@ -390,7 +390,7 @@ static void launch_backward_slots(const BwdArgs& a, const FaceRec* recs, const i
                                   const int32_t* count) {
     backward_slots<SETTINGS><<<(unsigned)a.L.bins, kBwdThreads, 0, a.stream>>>(
         recs, order, count, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx, (int32_t)a.L.nby,
-        a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V <= (int64_t)INT32_MAX ? 1 : 0);
+        a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V - 1 <= kTableMaxId ? 1 : 0);
 }
 
 hipError_t launch_backward(const BwdArgs& a) {

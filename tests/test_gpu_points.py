@@ -148,3 +148,23 @@ def test_points_autograd(dmr):
     np.testing.assert_array_equal(idx.cpu().numpy(), ref[0])
     refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, ref[0], g["zbuf"], g["dists"])
     assert rel_l2(p.grad.cpu().numpy(), refg) <= 1e-5
+
+
+@pytest.mark.parametrize("scale", [1e-10, 1e-8, 1e-6, 1e6])
+def test_points_backward_gradient_scales(dmr, scale):
+    """The point backward shares the per-tile fixed-point table: its accuracy
+    must not depend on the scale of the upstream gradients (all coordinates,
+    and the depth coordinates alone)."""
+    w = make_point_workload("points_small")
+    say(f"[gpu] points backward with upstream gradients scaled by {scale}")
+    out, (p, o), ws = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    g = {k: (a * np.float32(scale)).astype(np.float32) for k, a in point_upstream_grads(w).items()}
+    gp = torch.empty_like(p)
+    dmr.rasterize_points_bwd(p, o, w.H, w.W, w.K, out[0], to_dev(g["zbuf"]), to_dev(g["dists"]), gp)
+    refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, out[0].cpu().numpy(), g["zbuf"],
+                                     g["dists"])
+    got = gp.cpu().numpy()
+    err, err_z = rel_l2(got, refg), rel_l2(got[:, 2], refg[:, 2])
+    say(f"  rel L2 = {err:.2e}, depth coordinates {err_z:.2e}")
+    assert np.linalg.norm(refg[:, 2]) > 0
+    assert err <= 1e-5 and err_z <= 1e-5, (err, err_z)
