@@ -3,6 +3,7 @@
 #include <math.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <vector>
 
@@ -20,7 +21,6 @@ struct Pending {
 };
 
 struct Timing {
-    uint32_t mask = 0;   // bit id set: kernel id is timed
     std::vector<Pending> pending[kKernelCount];
     std::vector<hipEvent_t> pool;
     double total_ms[kKernelCount] = {};
@@ -28,8 +28,12 @@ struct Timing {
     hipEvent_t open_start[kKernelCount] = {};
 };
 
+// The bookkeeping below is shared by every host thread that launches
+// kernels: it is only touched under g_timing_mu. The mask (bit id set:
+// kernel id is timed) is read without the lock on every launch.
 Timing g_timing;
 std::mutex g_timing_mu;
+std::atomic<uint32_t> g_timing_mask{0};
 
 const char* const kKernelNames[kKernelCount] = {
     "zero_fwd", "face_setup_count", "bin_scan", "bin_fill", "bin_sort", "fine_raster", "zero_grad", "backward_slots",
@@ -66,13 +70,16 @@ hipError_t drain(int id) {
 }  // namespace
 
 void timing_begin(KernelId id, hipStream_t s) {
-    if (!(g_timing.mask >> id & 1u)) return;
+    if (!(g_timing_mask.load(std::memory_order_relaxed) >> id & 1u)) return;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
     hipEvent_t e = take_event();
     if (e && hipEventRecord(e, s) == hipSuccess) g_timing.open_start[id] = e;
 }
 
 void timing_end(KernelId id, hipStream_t s) {
-    if (!(g_timing.mask >> id & 1u) || !g_timing.open_start[id]) return;
+    if (!(g_timing_mask.load(std::memory_order_relaxed) >> id & 1u)) return;
+    std::lock_guard<std::mutex> lk(g_timing_mu);
+    if (!g_timing.open_start[id]) return;
     hipEvent_t e = take_event();
     if (e && hipEventRecord(e, s) == hipSuccess) g_timing.pending[id].push_back({g_timing.open_start[id], e});
     g_timing.open_start[id] = nullptr;
@@ -408,14 +415,14 @@ const char* dmr_kernel_name(int32_t id) {
 
 dmr_status dmr_set_kernel_timing(int32_t enable) {
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_timing.mask = enable != 0 ? (1u << kKernelCount) - 1u : 0u;
+    g_timing_mask.store(enable != 0 ? (1u << kKernelCount) - 1u : 0u);
     return DMR_SUCCESS;
 }
 
 dmr_status dmr_set_kernel_timing_mask(uint32_t mask) {
     if (mask >> kKernelCount) return DMR_ERROR_INVALID_VALUE;
     std::lock_guard<std::mutex> lk(g_timing_mu);
-    g_timing.mask = mask;
+    g_timing_mask.store(mask);
     return DMR_SUCCESS;
 }
 

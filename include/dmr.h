@@ -320,8 +320,10 @@ const char* dmr_status_string(dmr_status s);
  * kernel `id` (0 .. dmr_kernel_count()-1) is bracketed with HIP events on
  * the stream it runs on; dmr_kernel_timing() synchronises on the recorded
  * events and returns the summed duration (ms) and number of launches since
- * the last reset. Disabled by default; timing is process-wide and not
- * thread-safe.
+ * the last reset. Disabled by default; timing is process-wide. Launches
+ * from several host threads are recorded safely (the bookkeeping is
+ * serialised), but a kernel launched concurrently on two streams pairs its
+ * start and stop events per launch only when the launches do not overlap.
  */
 int32_t dmr_kernel_count(void);
 const char* dmr_kernel_name(int32_t id);
