@@ -39,7 +39,9 @@ EXPORTED = [
     "dmr_kernel_name", "dmr_set_kernel_timing", "dmr_set_kernel_timing_mask", "dmr_kernel_timing",
     "dmr_reset_kernel_timing", "dmr_blend_fwd", "dmr_blend_bwd", "dmr_project_fwd", "dmr_project_bwd",
     "rasterize_points_fwd", "rasterize_points_bwd", "dmr_points_workspace_min_size", "dmr_points_workspace_size_hint",
+    "rasterize_meshes_fwd_noalloc",
 ]
+DMR_NOALLOC_SCRATCH_BYTES = 128 << 20
 
 
 class DmrError(RuntimeError):
@@ -79,6 +81,8 @@ def lib(path: Optional[str] = None):
     L.rasterize_meshes_fwd_ex.restype = ctypes.c_int
     L.rasterize_meshes_fwd_ex.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float,
                                           P, P, P, P, P, SZ, ctypes.c_uint32, P]
+    L.rasterize_meshes_fwd_noalloc.restype = ctypes.c_int
+    L.rasterize_meshes_fwd_noalloc.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P, P, P]
     L.rasterize_meshes_bwd.restype = ctypes.c_int
     L.rasterize_meshes_bwd.argtypes = [P, I64, P, I64, P, I64, I32, I32, I32, ctypes.c_float, P, P, P, P, P, P, SZ,
                                        ctypes.c_uint32, P]
@@ -195,6 +199,31 @@ def rasterize_meshes_fwd_ex(verts: torch.Tensor, faces: torch.Tensor, mesh_face_
     DMR_RASTER_* bits; include/dmr.h)."""
     _forward(verts, faces, mesh_face_offsets, H, W, K, blur_radius, pix_to_face, zbuf, bary, dists, workspace,
              int(flags))
+
+
+def rasterize_meshes_fwd_noalloc(verts: torch.Tensor, faces: torch.Tensor, mesh_face_offsets: torch.Tensor,
+                                 H: int, W: int, K: int, blur_radius: float,
+                                 pix_to_face: torch.Tensor, zbuf: torch.Tensor, bary: torch.Tensor,
+                                 dists: torch.Tensor) -> None:
+    """C-ABI forward call that allocates nothing: the library's per-device
+    scratch array stands in for the workspace (include/dmr.h). Calls that
+    overlap on one device race."""
+    dev = verts.device
+    N = mesh_face_offsets.shape[0] - 1
+    _check(verts, "verts", torch.float32, dev)
+    _check(faces, "faces", torch.int64, dev)
+    _check(mesh_face_offsets, "mesh_face_offsets", torch.int64, dev)
+    shape = (N, H, W, K)
+    _check(pix_to_face, "pix_to_face", torch.int64, dev, shape)
+    _check(zbuf, "zbuf", torch.float32, dev, shape)
+    _check(bary, "bary", torch.float32, dev, shape + (3,))
+    _check(dists, "dists", torch.float32, dev, shape)
+    rc = lib().rasterize_meshes_fwd_noalloc(_ptr(verts), verts.shape[0], _ptr(faces), faces.shape[0],
+                                            _ptr(mesh_face_offsets), N, H, W, K, float(blur_radius),
+                                            _ptr(pix_to_face), _ptr(zbuf), _ptr(bary), _ptr(dists),
+                                            _stream_handle(dev))
+    if rc != 0:
+        raise DmrError("rasterize_meshes_fwd_noalloc", rc)
 
 
 def _forward(verts, faces, mesh_face_offsets, H, W, K, blur_radius, pix_to_face, zbuf, bary, dists, workspace,

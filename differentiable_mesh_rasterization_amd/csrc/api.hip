@@ -190,6 +190,72 @@ dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t*
     return launch_forward(a) == hipSuccess ? DMR_SUCCESS : DMR_ERROR_HIP;
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// allocation-free forward: its workspace is a file-scope device array
+// ---------------------------------------------------------------------------
+// Every device the library runs on holds its own copy of `scratch` until the
+// process ends. Host code never passes the array's name to a kernel or a
+// copy (on the host it only stands for the symbol): the device address is
+// looked up once per device with hipGetSymbolAddress and used from then on.
+static __device__ __align__(256) unsigned char scratch[DMR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// This device's `scratch`: the device of `stream` (the current device for
+// the null stream), looked up on first use with that device current.
+dmr_status scratch_for(hipStream_t stream, void** out) {
+    int dev = 0;
+    if (stream == nullptr) {
+        if (hipGetDevice(&dev) != hipSuccess) return DMR_ERROR_HIP;
+    } else if (hipStreamGetDevice(stream, &dev) != hipSuccess) {
+        return DMR_ERROR_HIP;
+    }
+    if (dev < 0 || dev >= kMaxScratchDevices) return DMR_ERROR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        int cur = 0;
+        if (hipGetDevice(&cur) != hipSuccess) return DMR_ERROR_HIP;
+        if (cur != dev && hipSetDevice(dev) != hipSuccess) return DMR_ERROR_HIP;
+        void* p = nullptr;
+        const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (cur != dev && hipSetDevice(cur) != hipSuccess) return DMR_ERROR_HIP;
+        if (err != hipSuccess || p == nullptr) return DMR_ERROR_HIP;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return DMR_SUCCESS;
+}
+
+}  // namespace
+
+extern "C" {
+
+dmr_status rasterize_meshes_fwd_noalloc(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                        const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W,
+                                        int32_t K, float blur_radius, int64_t* pix_to_face, float* zbuf, float* bary,
+                                        float* dists, hipStream_t stream) {
+    int64_t slots = 0;
+    dmr_status st = check_geometry(verts, V, faces, F, mesh_face_offsets, N, H, W, K, &slots);
+    if (st != DMR_SUCCESS) return st;
+    if (!isfinite(blur_radius) || blur_radius < 0.0f) return DMR_ERROR_INVALID_VALUE;
+    if (slots == 0) return DMR_SUCCESS;
+    if (!pix_to_face || !zbuf || !bary || !dists) return DMR_ERROR_INVALID_VALUE;
+    // face records and bin tables must fit; bin lists that do not fit take
+    // the exact full-face-range path, as with any small workspace
+    if (fwd_layout(N, F, H, W).min_bytes > (size_t)DMR_NOALLOC_SCRATCH_BYTES) return DMR_ERROR_UNSUPPORTED;
+    void* ws = nullptr;
+    st = scratch_for(stream, &ws);
+    if (st != DMR_SUCCESS) return st;
+    return rasterize_meshes_fwd_ex(verts, V, faces, F, mesh_face_offsets, N, H, W, K, blur_radius, pix_to_face,
+                                   zbuf, bary, dists, ws, (size_t)DMR_NOALLOC_SCRATCH_BYTES, 0u, stream);
+}
+
 dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* faces, int64_t F,
                                 const int64_t* mesh_face_offsets, int64_t N, int32_t H, int32_t W, int32_t K,
                                 float blur_radius, const int64_t* pix_to_face, const float* grad_zbuf,

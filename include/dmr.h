@@ -132,6 +132,30 @@ dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t*
                                    void* workspace, size_t workspace_bytes, uint32_t flags, hipStream_t stream);
 
 /*
+ * Allocation-free forward pass, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc): rasterize_meshes_fwd with the workspace replaced by a
+ * device array of DMR_NOALLOC_SCRATCH_BYTES that the library holds on each
+ * device it runs on until the process ends. Arguments and results are those
+ * of rasterize_meshes_fwd (settings 0); the call allocates nothing.
+ *   Sizes whose face records and bin tables (dmr_workspace_min_size) exceed
+ *   DMR_NOALLOC_SCRATCH_BYTES give DMR_ERROR_UNSUPPORTED before anything is
+ *   launched; bin lists that do not fit in the rest of the array take the
+ *   exact full-face-range path, so results never depend on the size.
+ *   Every call on a device shares that device's array: calls that overlap on
+ *   one device (different streams, or host threads) race and give undefined
+ *   results; calls ordered on one stream are safe. A backward pass of these
+ *   outputs runs without the forward's workspace (flags without
+ *   DMR_BWD_REUSE_FORWARD_WORKSPACE), which allocates nothing either.
+ */
+#define DMR_NOALLOC_SCRATCH_BYTES (128u << 20)
+dmr_status rasterize_meshes_fwd_noalloc(const float* verts, int64_t V, const int64_t* faces, int64_t F,
+                                        const int64_t* mesh_face_offsets, int64_t N,
+                                        int32_t H, int32_t W, int32_t K, float blur_radius,
+                                        int64_t* pix_to_face, float* zbuf, float* bary, float* dists,
+                                        hipStream_t stream);
+
+/*
  * Backward pass: maps the gradients of zbuf, bary and dists to vertex
  * positions (rocketrecap summary, "3:52 Differentiable Renderer": gradients
  * flow from image pixels back to the 3D parameters).
