@@ -61,9 +61,11 @@ def _check(ref_rgba, got_rgba, ref_g=None, got_g=None, scales=None):
 
 
 # A sigma far below the blur radius: outside faces get coverage weights that
-# underflow binary32 (exp(-d / sigma) with d / sigma up to 333), so a pixel
-# reached only by such faces has every weight, and a far background, below
-# the smallest float. The log-domain sums must still give their ratio.
+# underflow binary32 (exp(-d / sigma) with d / sigma up to 333 at a blur
+# radius of 1e-4, and 3333 at 1e-3, where they underflow binary64 too), so a
+# pixel reached only by such faces has every weight, and a far background,
+# below the smallest float. Both sides sum in the log domain and must still
+# give the ratio.
 VERY_SHARP = BlendParams(sigma=3e-7, gamma=1e-5, znear=1.0, zfar=100.0, eps=1e-10, background=(0.3, 0.6, 0.1))
 
 
@@ -71,8 +73,6 @@ VERY_SHARP = BlendParams(sigma=3e-7, gamma=1e-5, znear=1.0, zfar=100.0, eps=1e-1
 @pytest.mark.parametrize("name", ["sphere64", "spheres8_137", "small_hetero", "small_soups"])
 def test_blend_full_image(dmr, name, pname):
     w = make_workload(name)
-    if pname == "very_sharp" and w.blur > 1e-4:
-        pytest.skip("d / sigma would overflow the binary64 oracle too")
     prm = VERY_SHARP if pname == "very_sharp" else PARAMS[pname]
     say(f"[gpu] blend {name} {pname}")
     g = GpuCase.from_workload(w)
