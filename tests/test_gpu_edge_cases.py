@@ -5,8 +5,9 @@ a blur radius covering the image, off-screen faces, one face over every bin,
 thousands of faces in one bin, heavy bins split into quarter items, hundreds
 of faces each covering every pixel (whole and split bins), subnormal depths,
 faces using another mesh's vertices, the largest image side, hundreds of
-small meshes, invalid vertex indices, and the hand-worked cases; every case
-also through the backward pass."""
+small meshes, near-degenerate slivers (tiny non-zero doubled area), invalid
+vertex indices, and the hand-worked cases; every case also through the
+backward pass."""
 
 import json
 import os
@@ -250,6 +251,50 @@ def many_small_meshes():
     sizes = rng.integers(0, 4, 600)
     v, f = _soup(22, int(sizes.sum()), sigma=0.3)
     return v, f, np.concatenate([[0], np.cumsum(sizes)]), 8, 8, 2, 1e-2
+
+
+def _slivers(seed, F):
+    """Near-degenerate slivers: v2 continues the segment v0 -> v1 to twice
+    its length and is then moved by a few units in the last place, so the
+    binary32 doubled area A is tiny but non-zero (1e-9 down to about 1e-13;
+    v0 is drawn at scales 1e-3 to 0.3 around the image centre, where the
+    last place of a coordinate is small). Their raw barycentrics at a pixel
+    are edge functions of O(0.1) size divided by A: the rounding noise of the
+    edge functions can give every barycentric a positive sign at pixel
+    centres far outside the sliver, where only the bounding-box clause of the
+    inside test keeps the face out."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    f32 = np.float32
+    n = 8 * F
+    scale = 10.0 ** rng.uniform(-3.0, -0.5, (n, 1))
+    a = (scale * rng.uniform(-1.0, 1.0, (n, 2))).astype(f32)
+    t = rng.uniform(0.0, 2.0 * np.pi, n)
+    d = (rng.uniform(0.02, 0.4, (n, 1)) * np.stack([np.cos(t), np.sin(t)], 1)).astype(f32)
+    b = (a + d).astype(f32)
+    c = (a + f32(2) * d).astype(f32)
+    nudge = rng.integers(-3, 4, (n, 2)).astype(f32)
+    c = (c + nudge * np.spacing(np.abs(c)).astype(f32)).astype(f32)
+    x0, y0, x1, y1, x2, y2 = a[:, 0], a[:, 1], b[:, 0], b[:, 1], c[:, 0], c[:, 1]
+    A = (x1 - x0) * (y2 - y0) - (y1 - y0) * (x2 - x0)   # binary32, in the conventions' order
+    assert A.dtype == np.float32
+    keep = np.nonzero((np.abs(A) > 0) & (np.abs(A) < 1e-9))[0][:F]
+    assert len(keep) == F and np.abs(A[keep]).min() < 1e-11 and (np.abs(A[keep]) < 1e-10).sum() > F // 10
+    z = rng.uniform(1.0, 3.0, (F, 3)).astype(f32)
+    v = np.stack([np.concatenate([a[keep], z[:, :1]], 1), np.concatenate([b[keep], z[:, 1:2]], 1),
+                  np.concatenate([c[keep], z[:, 2:]], 1)], 1).astype(f32)
+    return v.reshape(-1, 3), np.arange(3 * F).reshape(F, 3)
+
+
+@case
+def near_degenerate_slivers():
+    v, f = _slivers(23, 400)
+    return v, f, [0, 400], 64, 64, 3, 0.0
+
+
+@case
+def near_degenerate_slivers_blur():
+    v, f = _slivers(24, 400)
+    return v, f, [0, 400], 48, 56, 4, 1e-4
 
 
 @pytest.mark.parametrize("name", list(CASES))
