@@ -147,3 +147,46 @@ def rel_l2(a, b):
     b = np.asarray(b, np.float64)
     den = np.linalg.norm(b)
     return float(np.linalg.norm(a - b) / (den if den > 0 else 1.0))
+
+
+def region_faces(verts, faces, offsets, n, H, W, blur, i0, i1, j0, j1, margin=1e-3):
+    """Global ids (ascending) of mesh n's faces whose box, grown by
+    sqrt(blur_radius) + margin, reaches the pixel centres of rows [i0, i1)
+    and columns [j0, j1). A face outside that box is neither strictly inside
+    at those pixels nor within sqrt(blur_radius) of them, so it cannot be a
+    candidate there; the margin, far above binary32 rounding, keeps the
+    selection conservative."""
+    f0, f1 = int(offsets[n]), int(offsets[n + 1])
+    tri = np.asarray(verts, np.float64)[np.asarray(faces[f0:f1], np.int64)]
+    r = np.sqrt(blur) + margin
+    xl = (2.0 * j0 + 1.0) / W - 1.0
+    xh = (2.0 * (j1 - 1) + 1.0) / W - 1.0
+    yl = (2.0 * i0 + 1.0) / H - 1.0
+    yh = (2.0 * (i1 - 1) + 1.0) / H - 1.0
+    keep = ((tri[..., 0].min(1) - r <= xh) & (tri[..., 0].max(1) + r >= xl)
+            & (tri[..., 1].min(1) - r <= yh) & (tri[..., 1].max(1) + r >= yl))
+    return f0 + np.nonzero(keep)[0]
+
+
+def oracle_region(oracle, verts, faces, offsets, n, H, W, K, blur, i0, i1, j0, j1, grads=None):
+    """The oracle on the pixels of rows [i0, i1) x columns [j0, j1) of image
+    n, run on the faces that can reach them (region_faces): the kept faces
+    form one mesh in their global order, so depth ties break as in the
+    whole batch, and their local indices map back to global ids.
+
+    Returns (flat global pixel ids in row-major order, (pix_to_face, zbuf,
+    bary, dists) for those pixels, and, with grads = (gz, gb, gd) shaped
+    like the outputs (or None each), the oracle's grad_verts [V, 3] over
+    them)."""
+    kept = region_faces(verts, faces, offsets, n, H, W, blur, i0, i1, j0, j1)
+    sub = np.ascontiguousarray(np.asarray(faces, np.int64)[kept])
+    ii, jj = np.meshgrid(np.arange(i0, i1), np.arange(j0, j1), indexing="ij")
+    local = (ii * W + jj).reshape(-1).astype(np.int64)
+    sub_off = np.array([0, len(kept)], np.int64)
+    p2f, zb, ba, ds = oracle.rasterize(verts, sub, sub_off, H, W, K, blur, pixels=local)
+    glob = np.append(kept, -1)[np.where(p2f >= 0, p2f, len(kept))]
+    gv = None
+    if grads is not None:
+        gz, gb, gd = grads
+        gv = oracle.backward(verts, sub, sub_off, H, W, K, blur, p2f, gz, gb, gd, pixels=local)
+    return n * H * W + local, (glob, zb, ba, ds), gv
