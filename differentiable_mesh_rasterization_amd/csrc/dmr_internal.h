@@ -30,6 +30,17 @@ constexpr int kSetupThreads = 256;
 constexpr int kSortMax = 4096;
 constexpr int kSortMin = kFineThreads;
 constexpr int kRoundsPerBin = kSortMax / kFineThreads;
+// The setup passes count faces into kCountReplicas copies of the bin counts
+// (workgroup w into copy w % kCountReplicas), so that a bin's global atomics
+// from many workgroups spread over several addresses; the scan adds the
+// copies, and the fill places each copy's faces after those of the copies
+// before it (the same workgroup-to-copy rule in the setup and fill).
+constexpr int kCountReplicas = 8;
+// Copies used for a given number of bins: with many bins each one sees few
+// workgroups and the scan's cost of adding copies dominates.
+__host__ __device__ __forceinline__ int32_t count_replicas(int64_t bins) {
+    return bins <= 8192 ? kCountReplicas : 1;
+}
 
 // Whether a bin list (offset o, cnt entries) is in the workspace and
 // depth-sorted with round bounds.
@@ -116,7 +127,7 @@ static_assert(sizeof(WsHeader) == 256, "WsHeader layout");
 struct FwdLayout {
     int64_t bins, nbx, nby;
     int64_t setup_blocks;
-    size_t off_records, off_fbin, off_count, off_offset, off_cursor, off_perm, off_items, off_live, off_roundlb,
+    size_t off_records, off_fbin, off_count, off_offset, off_rep, off_perm, off_items, off_live, off_roundlb,
         off_entries;
     size_t min_bytes;
 };
@@ -139,8 +150,8 @@ inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W, size_t r
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
     L.off_offset = o;
     o = align_up(o + (size_t)(L.bins + 1) * sizeof(int64_t), 256);
-    L.off_cursor = o;
-    o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
+    L.off_rep = o;   // kCountReplicas x bins: per-copy counts, then per-copy fill cursors
+    o = align_up(o + (size_t)kCountReplicas * L.bins * sizeof(int32_t), 256);
     L.off_perm = o;
     o = align_up(o + (size_t)L.bins * sizeof(int32_t), 256);
     L.off_items = o;

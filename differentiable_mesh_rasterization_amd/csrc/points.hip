@@ -43,7 +43,8 @@ constexpr int kPointHistBins = 4096;
 __global__ __launch_bounds__(kSetupThreads) void point_setup_count(
     const float* __restrict__ pts, int64_t P, const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W,
     float radius, int32_t nbx, int32_t nby, PointRec* __restrict__ recs, FaceBin* __restrict__ fbin,
-    int32_t* __restrict__ bin_count, int32_t* __restrict__ block_live) {
+    int32_t* __restrict__ rep_count, int32_t replicas, int64_t bins, int32_t* __restrict__ block_live) {
+    int32_t* __restrict__ bin_count = rep_count + (int64_t)(blockIdx.x % (uint32_t)replicas) * bins;
     __shared__ int32_t hist[kPointHistBins];
     __shared__ int64_t home_s, home_lo, home_hi;
     __shared__ int32_t live_s;
@@ -129,7 +130,7 @@ hipError_t launch_point_setup(const FwdArgs& a, PointRec* recs, FaceBin* fbin, i
     timing_begin(kKPointSetup, a.stream);
     point_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
         a.points, a.F, a.off, a.N, a.H, a.W, a.radius, (int32_t)a.L.nbx, (int32_t)a.L.nby, recs, fbin, count,
-        block_live);
+        count_replicas(a.L.bins), a.L.bins, block_live);
     timing_end(kKPointSetup, a.stream);
     return hipGetLastError();
 }

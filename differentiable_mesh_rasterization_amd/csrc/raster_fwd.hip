@@ -49,8 +49,10 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
     const float* __restrict__ verts, int64_t V, const int64_t* __restrict__ faces, int64_t F,
     const int64_t* __restrict__ off, int64_t N, int32_t H, int32_t W, float blur, uint32_t settings,
     int32_t nbx, int32_t nby, FaceRec* __restrict__ recs, FaceBin* __restrict__ fbin,
-    int32_t* __restrict__ bin_count, int32_t* __restrict__ block_live, WsHeader* __restrict__ hdr) {
+    int32_t* __restrict__ rep_count, int32_t replicas, int64_t bins, int32_t* __restrict__ block_live,
+    WsHeader* __restrict__ hdr) {
     __shared__ int32_t hist[kHistBins];
+    int32_t* __restrict__ bin_count = rep_count + (int64_t)(blockIdx.x % (uint32_t)replicas) * bins;
     __shared__ int64_t home_s, home_lo, home_hi;
     __shared__ int32_t live_s;
     const int per_img = nbx * nby;
@@ -175,8 +177,8 @@ __global__ __launch_bounds__(kSetupThreads) void face_setup_count(
 
 // ---------------------------------------------------------------------------
 // K2: exclusive prefix sum of the bin counts (one workgroup), header stats,
-// cursor reset, the order in which the sort visits the bins, and the work
-// items of the fine pass. Both orders put the heaviest work first (counting
+// the fill cursors, the order in which the sort visits the bins, and the
+// work items of the fine pass. Both orders put the heaviest work first (counting
 // sort on floor(log2(weight)) buckets), so that long workgroups start early
 // and do not form the kernel's tail. A bin with at least kSplitMin faces
 // (when K allows) gives four quarter items of a quarter of its weight.
@@ -229,9 +231,9 @@ __device__ __forceinline__ int64_t block_sum64(int64_t v, unsigned long long* ac
     return r;
 }
 
-__global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restrict__ count,
+__global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ count,
                                                          int64_t* __restrict__ offset,
-                                                         int32_t* __restrict__ cursor,
+                                                         int32_t* __restrict__ rep, int32_t replicas,
                                                          int32_t* __restrict__ perm, uint32_t* __restrict__ items,
                                                          int64_t bins, int32_t allow_split,
                                                          const int32_t* __restrict__ block_live,
@@ -251,6 +253,20 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
     if (t == 0) {
         acc_ovf = 0;
         acc_live = 0;
+    }
+    // each bin's count is the sum of its copies; their running sums become
+    // the copies' fill cursors (copy r's faces follow those of copies < r)
+    for (int64_t b = t; b < bins; b += kScanThreads) {
+        int32_t cr[kCountReplicas];
+#pragma unroll
+        for (int r = 0; r < kCountReplicas; ++r) cr[r] = r < replicas ? rep[(int64_t)r * bins + b] : 0;
+        int32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kCountReplicas; ++r) {
+            if (r < replicas) rep[(int64_t)r * bins + b] = c;
+            c += cr[r];
+        }
+        count[b] = c;
     }
     const int64_t per = (bins + kScanThreads - 1) / kScanThreads;
     const int64_t b0 = t * per;
@@ -293,7 +309,6 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
         const int32_t c = count[b];
         if (run + c > capacity) ++over;
         run += c;
-        cursor[b] = 0;
         perm[atomicAdd(&bucket_at[order_bucket(c)], 1)] = (int32_t)b;
         const uint32_t code = (uint32_t)b << 3;
         if (allow_split && c >= kSplitMin) {
@@ -328,9 +343,12 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(const int32_t* __restri
 __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restrict__ fbin, int64_t F,
                                                           const int32_t* __restrict__ count,
                                                           const int64_t* __restrict__ offset,
-                                                          int32_t* __restrict__ cursor,
+                                                          int32_t* __restrict__ rep, int32_t replicas, int64_t bins,
                                                           int32_t* __restrict__ entries, int64_t capacity,
                                                           int32_t nbx, int32_t nby) {
+    // this workgroup's copy of the cursors (the copy its setup workgroup
+    // counted into)
+    int32_t* __restrict__ cursor = rep + (int64_t)(blockIdx.x % (uint32_t)replicas) * bins;
     __shared__ int32_t hist[kHistBins];
     __shared__ int32_t base[kHistBins];
     __shared__ int64_t home_s;
@@ -1037,7 +1055,7 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     FaceBin* fbin = reinterpret_cast<FaceBin*>(ws + a.L.off_fbin);
     int32_t* count = reinterpret_cast<int32_t*>(ws + a.L.off_count);
     int64_t* offset = reinterpret_cast<int64_t*>(ws + a.L.off_offset);
-    int32_t* cursor = reinterpret_cast<int32_t*>(ws + a.L.off_cursor);
+    int32_t* rep = reinterpret_cast<int32_t*>(ws + a.L.off_rep);
     int32_t* perm = reinterpret_cast<int32_t*>(ws + a.L.off_perm);
     int32_t* block_live = reinterpret_cast<int32_t*>(ws + a.L.off_live);
     float* round_lb = reinterpret_cast<float*>(ws + a.L.off_roundlb);
@@ -1046,31 +1064,34 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     // header + bin counts to zero (header words are int32-sized multiples)
     {
         timing_begin(kKZeroFwd, a.stream);
-        zero_i32x2<<<(unsigned)std::min<int64_t>(1024, (a.L.bins + 255) / 256 + 1), 256, 0, a.stream>>>(
-            reinterpret_cast<int32_t*>(hdr), (int64_t)(sizeof(WsHeader) / 4), count, a.L.bins);
+        const int64_t nrep = (int64_t)count_replicas(a.L.bins) * a.L.bins;
+        zero_i32x2<<<(unsigned)std::min<int64_t>(1024, (nrep + 255) / 256 + 1), 256, 0, a.stream>>>(
+            reinterpret_cast<int32_t*>(hdr), (int64_t)(sizeof(WsHeader) / 4), rep, nrep);
         timing_end(kKZeroFwd, a.stream);
     }
     if (a.F > 0 && a.points) {
-        hipError_t err = launch_point_setup(a, reinterpret_cast<PointRec*>(recs), fbin, count, block_live, hdr);
+        hipError_t err = launch_point_setup(a, reinterpret_cast<PointRec*>(recs), fbin, rep, block_live, hdr);
         if (err != hipSuccess) return err;
     } else if (a.F > 0) {
         timing_begin(kKFaceSetup, a.stream);
         face_setup_count<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
             a.verts, a.V, a.faces, a.F, a.off, a.N, a.H, a.W, a.blur, a.settings, (int32_t)a.L.nbx,
-            (int32_t)a.L.nby, recs, fbin, count, block_live, hdr);
+            (int32_t)a.L.nby, recs, fbin, rep, count_replicas(a.L.bins), a.L.bins, block_live, hdr);
         timing_end(kKFaceSetup, a.stream);
     }
     timing_begin(kKBinScan, a.stream);
     uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
     // heavy bins are split into quarter items for the mesh fine pass only
     const int split = (a.K <= kSplitMaxK && !a.points) ? 1 : 0;
-    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, cursor, perm, items, a.L.bins, split, block_live,
+    bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, rep, count_replicas(a.L.bins), perm, items, a.L.bins,
+                                                 split, block_live,
                                                  a.F > 0 ? a.L.setup_blocks : 0, a.capacity, a.L.min_bytes, hdr);
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {
         timing_begin(kKBinFill, a.stream);
         bin_fill<<<(unsigned)((a.F + kSetupThreads - 1) / kSetupThreads), kSetupThreads, 0, a.stream>>>(
-            fbin, a.F, count, offset, cursor, entries, a.capacity, (int32_t)a.L.nbx, (int32_t)a.L.nby);
+            fbin, a.F, count, offset, rep, count_replicas(a.L.bins), a.L.bins, entries, a.capacity, (int32_t)a.L.nbx,
+            (int32_t)a.L.nby);
         timing_end(kKBinFill, a.stream);
     }
     if (a.F > 0 && sort) {
