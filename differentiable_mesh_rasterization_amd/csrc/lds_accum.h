@@ -168,17 +168,22 @@ __device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (
 }
 
 // Flushes a workgroup's table into grad (3 floats per id) with float atomics.
+// Consecutive lanes take consecutive floats of the table (entry j / 3,
+// coordinate j % 3), so that the three coordinates of an id, and the ids of
+// neighbouring entries when they are neighbours in grad, reach memory in the
+// same wave-wide atomic instruction: fewer cache lines per instruction than
+// one entry per lane with a separate instruction per coordinate.
 template <int HB = kHashBits>
 __device__ __forceinline__ void flush_table(const uint32_t* hkey, const unsigned long long (*hval)[3],
                                             float* __restrict__ grad, int nthreads) {
-    for (int e = threadIdx.x; e < (1 << HB); e += nthreads) {
+    static_assert(HB <= 14, "division by multiplication");
+    for (int j = threadIdx.x; j < 3 * (1 << HB); j += nthreads) {
+        const int e = (int)(((uint32_t)j * 0xAAABu) >> 17);   // j / 3, exact for j < 3 * 2^14
+        const int c = j - 3 * e;
         const uint32_t key = hkey[e];
         if (key != kEmptyKey) {
             const int64_t vid = (int64_t)(key & kIdMask);
-            const uint32_t ec = key >> kIdBits;
-            atomicAdd(&grad[3 * vid + 0], from_fixed(hval[e][0], ec));
-            atomicAdd(&grad[3 * vid + 1], from_fixed(hval[e][1], ec));
-            atomicAdd(&grad[3 * vid + 2], from_fixed(hval[e][2], ec));
+            atomicAdd(&grad[3 * vid + c], from_fixed(hval[e][c], key >> kIdBits));
         }
     }
 }
