@@ -93,7 +93,17 @@ __device__ __forceinline__ int table_find(uint32_t* hkey, uint32_t id, uint32_t 
     }
 }
 
-__device__ __forceinline__ uint32_t hash_slot0(uint32_t id, int hb) { return (id * 2654435761u) >> (32 - hb); }
+// First probe slot of `id` in a table of 2^hb entries: a multiplicative hash
+// of id >> run_bits with the low run_bits of the id kept, so that a run of
+// 2^run_bits consecutive ids takes consecutive slots (run_bits = 0: a plain
+// multiplicative hash of the id). Consecutive slots are flushed by
+// consecutive lanes, so runs of ids that are neighbours in grad reach memory
+// in the same atomic instruction; the price is longer probe sequences when
+// the table is well filled, so callers keep run_bits = 0 unless the ids of
+// one workgroup come in runs.
+__device__ __forceinline__ uint32_t hash_slot0(uint32_t id, int hb, int run_bits) {
+    return ((((id >> run_bits) * 2654435761u) >> (32 - hb + run_bits)) << run_bits) | (id & ((1u << run_bits) - 1u));
+}
 
 __device__ __forceinline__ void global_add3(float* __restrict__ grad, int64_t vi, float gx, float gy, float gz) {
     atomicAdd(&grad[3 * vi + 0], gx);
@@ -108,14 +118,14 @@ __device__ __forceinline__ void global_add3(float* __restrict__ grad, int64_t vi
 template <int HB = kHashBits>
 __device__ __forceinline__ void vertex_add(uint32_t* hkey, unsigned long long (*hval)[3],
                                            float* __restrict__ grad, int64_t vi, float gx, float gy, float gz,
-                                           bool use_hash) {
+                                           bool use_hash, int run_bits = 0) {
     const float m = fmaxf(fabsf(gx), fmaxf(fabsf(gy), fabsf(gz)));   // fmaxf drops a NaN operand
     const uint32_t code = mag_code(m);
     const bool nan = (gx != gx) || (gy != gy) || (gz != gz);
     if (code == 0u && !nan) return;   // three zeros: nothing to add
     if (use_hash && m <= 3.402823466e38f && !nan) {
         const uint32_t id = (uint32_t)vi;
-        const uint32_t h = hash_slot0(id, HB);
+        const uint32_t h = hash_slot0(id, HB, run_bits);
         const uint32_t first = atomicCAS(&hkey[h], kEmptyKey, id | (code << kIdBits));
         uint32_t ec = 0;
         const int slot = table_find<HB>(hkey, id, code, h, first, ec);
@@ -136,7 +146,7 @@ __device__ __forceinline__ void vertex_add(uint32_t* hkey, unsigned long long (*
 template <int HB = kHashBits>
 __device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (*hval)[3],
                                             float* __restrict__ grad_verts, const int64_t (&vi)[3],
-                                            const float (&g)[9], bool use_hash) {
+                                            const float (&g)[9], bool use_hash, int run_bits) {
     uint32_t code[3], h[3], cur[3];
     bool elig[3], zero[3];
 #pragma unroll
@@ -148,7 +158,7 @@ __device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (
         zero[k] = code[k] == 0u && !nan;   // three zeros: nothing to add
         elig[k] = use_hash && !zero[k] && m <= 3.402823466e38f && !nan;
         const uint32_t id = (uint32_t)vi[k];
-        h[k] = hash_slot0(id, HB);
+        h[k] = hash_slot0(id, HB, run_bits);
         cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], kEmptyKey, id | (code[k] << kIdBits)) : 0u;
     }
 #pragma unroll

@@ -258,13 +258,13 @@ __device__ __forceinline__ void load_slot_rest(const FaceRec* __restrict__ recs,
 
 template <uint32_t SETTINGS>
 __device__ __forceinline__ void apply_slot(const SlotIn& in, uint32_t* hkey, unsigned long long (*hval)[3],
-                                           float* __restrict__ grad_verts, bool use_hash) {
+                                           float* __restrict__ grad_verts, bool use_hash, int run_bits) {
     if (!in.ok) return;
     PairState st;
     eval_pair(in.r, in.px, in.py, __builtin_inff(), true, SETTINGS, st);
     float g[9];
     slot_partials(in.r, st, in.px, in.py, in.gz, in.gb0, in.gb1, in.gb2, in.gd, SETTINGS, g);
-    vertex_add3(hkey, hval, grad_verts, in.vi, g, use_hash);
+    vertex_add3(hkey, hval, grad_verts, in.vi, g, use_hash, run_bits);
 }
 
 // One workgroup per tile: workgroup w takes bin w or, with the forward's
@@ -288,7 +288,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const float* __restrict__ verts, const int64_t* __restrict__ faces, int64_t V, int64_t F,
     int32_t H, int32_t W, int32_t K, int32_t nbx, int32_t nby, const int64_t* __restrict__ pix_to_face,
     const float* __restrict__ gzb, const float* __restrict__ gba, const float* __restrict__ gds,
-    float* __restrict__ grad_verts, int32_t use_hash_arg) {
+    float* __restrict__ grad_verts, int32_t use_hash_arg, int32_t soup_run_bits) {
     __shared__ uint32_t hkey[kHashSize];
     __shared__ unsigned long long hval[kHashSize][3];
     __shared__ int32_t lface[kListCap];
@@ -305,9 +305,16 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
     const uint32_t m_k = K > 1 ? 0xffffffffu / (uint32_t)K + 1u : 0u;
     const int tile_slots = kBin * row_slots;
     int64_t b = blockIdx.x;
+    int run_bits = 0;
     if (bin_order) {
         b = bin_order[b];
-        if (bin_count[b] == 0) return;   // no face, no filled slot
+        const int32_t c = bin_count[b];
+        if (c == 0) return;   // no face, no filled slot
+        // runs of ids only where the tile's vertices (at most three per
+        // face of its bin list) fit the table and each face has few slots
+        // (at most two on average), so that the flush's atomics outnumber
+        // the table's adds
+        if (3 * (int64_t)c <= kHashSize && (int64_t)K * kBinPixels <= 2 * (int64_t)c) run_bits = soup_run_bits;
     }
     const int64_t n = b / per_img;
     const int rem = (int)(b - n * per_img);
@@ -378,19 +385,30 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
                 }
             }
 #pragma unroll
-            for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash);
+            for (int u = 0; u < 2; ++u) apply_slot<SETTINGS>(in[u], hkey, hval, grad_verts, use_hash, run_bits);
         }
         __syncthreads();
     }
     flush_table(hkey, hval, grad_verts, kBwdThreads);
 }
 
+// Table slots for runs of 2^kSoupRunBits consecutive vertex ids when the
+// vertices mostly belong to one face each (V >= 2F, as in triangle soups,
+// where V = 3F): a tile's ids then come in runs (the three vertices of a
+// face are numbered together), and consecutive slots flush as contiguous
+// floats. Only tiles whose vertices fit the table and whose faces have few
+// slots each use it (runs lengthen the probe sequences of every add when
+// the table is well filled); meshes that share vertices keep the plain
+// hash.
+constexpr int kSoupRunBits = 3;
+
 template <uint32_t SETTINGS>
 static void launch_backward_slots(const BwdArgs& a, const FaceRec* recs, const int32_t* order,
                                   const int32_t* count) {
     backward_slots<SETTINGS><<<(unsigned)a.L.bins, kBwdThreads, 0, a.stream>>>(
         recs, order, count, a.verts, a.faces, a.V, a.F, a.H, a.W, a.K, (int32_t)a.L.nbx, (int32_t)a.L.nby,
-        a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V - 1 <= kTableMaxId ? 1 : 0);
+        a.pix_to_face, a.gz, a.gb, a.gd, a.grad_verts, a.V - 1 <= kTableMaxId ? 1 : 0,
+        a.V >= 2 * a.F ? kSoupRunBits : 0);
 }
 
 hipError_t launch_backward(const BwdArgs& a) {

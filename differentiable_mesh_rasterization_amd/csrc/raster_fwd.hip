@@ -720,6 +720,15 @@ __device__ __forceinline__ int block256_exclusive_sum_total(int v, int* wsum, in
     return before + x - v;
 }
 
+// A face record staged piece-major in LDS.
+__device__ __forceinline__ FaceRec staged_rec(const int4* s, uint32_t u) {
+    FaceRec r;
+    int4* d = reinterpret_cast<int4*>(&r);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) d[p] = s[p * kFineThreads + u];
+    return r;
+}
+
 // Pixel centre and current pruning bound of one owner of the fine pass.
 struct OwnerRec {
     float px, py;
@@ -740,8 +749,10 @@ struct OwnerRec {
 // K-th of any owner bounds the K-th of their union from above), and the
 // four lists are merged at the end.
 //
-// Each round stages up to 256 of the bin's faces in LDS (one per thread).
-// Every wave then describes the pixel boxes of its 64 faces with ballots:
+// Each round stages up to 256 of the bin's faces in LDS (one per thread),
+// piece-major (the 16-byte piece p of every record together), so that the
+// lanes of a wave reading the records of unrelated faces spread over the
+// LDS banks. Every wave then describes the pixel boxes of its 64 faces with ballots:
 // colmask[c] has bit u set when face slot u's box covers bin column c, and
 // rowmask[r] likewise for bin row r. An owner's candidate faces in the
 // round are colmask[its column] & rowmask[its row].
@@ -774,7 +785,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     // staged face records, their face indices and the owners' records; the
     // output phase reuses the whole block for its key exchange
     __shared__ __align__(16) unsigned char stage[kFineThreads * (sizeof(FaceRec) + 4 + sizeof(OwnerRec))];
-    FaceRec* srec = reinterpret_cast<FaceRec*>(stage);
+    int4* srec4 = reinterpret_cast<int4*>(stage);   // piece p of record u at [p * kFineThreads + u]
     int32_t* sface = reinterpret_cast<int32_t*>(stage + kFineThreads * sizeof(FaceRec));
     OwnerRec* orec = reinterpret_cast<OwnerRec*>(stage + kFineThreads * (sizeof(FaceRec) + 4));
     // the round's masks
@@ -866,7 +877,9 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 r1 = min((fb.box_hi >> 16) - by * kBin, reg_r + reg_w - 1);
                 live = (c0 <= c1) && (r0 <= r1);
                 if (live) {
-                    srec[t] = recs[fid];
+                    const int4* src = reinterpret_cast<const int4*>(recs + fid);
+#pragma unroll
+                    for (int p = 0; p < 4; ++p) srec4[p * kFineThreads + t] = src[p];
                     sface[t] = (int32_t)fid;
                 }
             }
@@ -932,7 +945,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                     const uint32_t pc = pcode[e];
                     const OwnerRec ow = orec[pc >> 8];
                     const double kk =
-                        pair_key<PERSP>(srec[pc & 255u], sface[pc & 255u], ow.px, ow.py, blur, ow.bound);
+                        pair_key<PERSP>(staged_rec(srec4, pc & 255u), sface[pc & 255u], ow.px, ow.py, blur, ow.bound);
                     if (key_bits(kk) != kEmptyKeyBits) pres[atomicAdd(&ofill[pc >> 8], 1)] = kk;
                 }
                 __syncthreads();
