@@ -337,8 +337,10 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
 // K3: bin fill
 // ---------------------------------------------------------------------------
 // Same privatisation as K1: the block counts its home-mesh entries per bin
-// in LDS, reserves each bin's range with one global atomic, then places its
-// faces at LDS-assigned positions inside the reserved ranges. The order of
+// in LDS, reserves each bin's range with one global atomic (a thread's
+// atomics for its bins are all issued before any result is waited for),
+// then places its faces inside the reserved ranges with LDS atomics on the
+// same counters, which now hold the ranges' starts. The order of
 // faces inside a bin list does not affect any result.
 __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restrict__ fbin, int64_t F,
                                                           const int32_t* __restrict__ count,
@@ -349,8 +351,7 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restr
     // this workgroup's copy of the cursors (the copy its setup workgroup
     // counted into)
     int32_t* __restrict__ cursor = rep + (int64_t)(blockIdx.x % (uint32_t)replicas) * bins;
-    __shared__ int32_t hist[kHistBins];
-    __shared__ int32_t base[kHistBins];
+    __shared__ int32_t hist[kHistBins];   // counts, then cursors
     __shared__ int64_t home_s;
     const int per_img = nbx * nby;
     const bool use_lds = per_img <= kHistBins;
@@ -376,10 +377,22 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restr
     if (use_lds) {
         __syncthreads();
         const int64_t hb = home * per_img;
-        for (int q = threadIdx.x; q < per_img; q += kSetupThreads) {
-            const int32_t c = hist[q];
-            if (c) base[q] = atomicAdd(&cursor[hb + q], c);
-            hist[q] = 0;
+        constexpr int kPerT = kHistBins / kSetupThreads;
+        int32_t c[kPerT], r[kPerT];
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const int q = threadIdx.x + k * kSetupThreads;
+            c[k] = q < per_img ? hist[q] : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const int q = threadIdx.x + k * kSetupThreads;
+            r[k] = c[k] ? atomicAdd(&cursor[hb + q], c[k]) : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPerT; ++k) {
+            const int q = threadIdx.x + k * kSetupThreads;
+            if (q < per_img) hist[q] = r[k];   // the block's start in the bin's range
         }
         __syncthreads();
     }
@@ -391,7 +404,7 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restr
             const int64_t gb = binbase + q;
             const int64_t o = offset[gb];
             int32_t pos;
-            if (local) pos = base[q] + atomicAdd(&hist[q], 1);
+            if (local) pos = atomicAdd(&hist[q], 1);
             else pos = atomicAdd(&cursor[gb], 1);
             if (o + count[gb] <= capacity) entries[o + pos] = (int32_t)f;
         }
