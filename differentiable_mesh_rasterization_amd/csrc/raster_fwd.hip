@@ -421,8 +421,6 @@ __global__ __launch_bounds__(kSetupThreads) void bin_fill(const FaceBin* __restr
 // list. Lists longer than kSortMax are left as they are (their bound is -inf).
 constexpr int kSortThreads = 256;
 constexpr int kSortBuckets = 1024;
-constexpr int kBucketsPer = kSortBuckets / kSortThreads;   // buckets per sort thread
-static_assert(kSortBuckets % kSortThreads == 0, "whole buckets per sort thread");
 
 __device__ __forceinline__ uint32_t float_order_bits(float x) {
     const uint32_t u = __float_as_uint(x);
@@ -453,6 +451,91 @@ __device__ __forceinline__ int block256_exclusive_sum(int v, int* wsum) {
     return before + x - v;
 }
 
+// Sorts one list of at most PER * kSortThreads entries over NB buckets (the
+// list held in registers: entry q = t + kSortThreads * i).
+template <int PER, int NB>
+__device__ __forceinline__ void sort_list(const FaceBin* __restrict__ fbin, int32_t* __restrict__ entries, int64_t o,
+                                          int32_t cnt, float* __restrict__ lb, int32_t* hist, int* wsum,
+                                          uint32_t& lo_s, uint32_t& hi_s, uint32_t* rmin) {
+    constexpr int BPT = NB / kSortThreads;   // buckets per thread
+    static_assert(NB % kSortThreads == 0 && NB <= kSortBuckets, "whole buckets per sort thread");
+    const int t = threadIdx.x;
+    if (t == 0) {
+        lo_s = 0xffffffffu;
+        hi_s = 0u;
+    }
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) hist[t * BPT + i] = 0;
+    if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
+    int32_t id[PER];
+    uint32_t zb[PER];   // order bits of zmin
+    uint32_t mylo = 0xffffffffu, myhi = 0u;
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int q = t + kSortThreads * i;
+        id[i] = q < cnt ? entries[o + q] : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int q = t + kSortThreads * i;
+        zb[i] = 0;
+        if (q < cnt) {
+            zb[i] = float_order_bits(__uint_as_float(fbin[id[i]].zmin_bits));
+            mylo = min(mylo, zb[i]);
+            myhi = max(myhi, zb[i]);
+        }
+    }
+    __syncthreads();
+    atomicMin(&lo_s, mylo);
+    atomicMax(&hi_s, myhi);
+    __syncthreads();
+    const float lo = order_bits_float(lo_s), hi = order_bits_float(hi_s);
+    const float scale = (hi > lo) ? (float)NB / (hi - lo) : 0.0f;
+    int bk[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        int k = (int)((order_bits_float(zb[i]) - lo) * scale);
+        k = k < 0 ? 0 : (k >= NB ? NB - 1 : k);
+        bk[i] = k;
+        if (t + kSortThreads * i < cnt) atomicAdd(&hist[k], 1);
+    }
+    __syncthreads();
+    // bucket starts: each thread owns BPT consecutive buckets
+    {
+        int c[BPT];
+        int local = 0;
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            c[i] = hist[t * BPT + i];
+            local += c[i];
+        }
+        int run = block256_exclusive_sum(local, wsum);
+#pragma unroll
+        for (int i = 0; i < BPT; ++i) {
+            hist[t * BPT + i] = run;
+            run += c[i];
+        }
+    }
+    __syncthreads();
+    // Every entry has been read: scatter the ids to their sorted places in
+    // the list, and note each round's smallest depth bound.
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        if (t + kSortThreads * i < cnt) {
+            const int pos = atomicAdd(&hist[bk[i]], 1);
+            entries[o + pos] = id[i];
+            atomicMin(&rmin[pos / kFineThreads], zb[i]);
+        }
+    }
+    __syncthreads();
+    // round r's bound: the smallest zmin of rounds r and later
+    if (t < kRoundsPerBin) {
+        uint32_t run = 0xffffffffu;
+        for (int r = t; r < kRoundsPerBin; ++r) run = min(run, rmin[r]);
+        lb[t] = (run == 0xffffffffu) ? __builtin_inff() : order_bits_float(run);
+    }
+}
+
 __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restrict__ fbin,
                                                          const int32_t* __restrict__ count,
                                                          const int64_t* __restrict__ offset,
@@ -466,82 +549,16 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
     const int64_t b = perm[blockIdx.x];
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
-    const int t = threadIdx.x;
     float* lb = round_lb + b * kRoundsPerBin;
     if (!list_sorted(o, cnt, capacity)) return;   // the fine passes read no bound of it
-    if (t == 0) {
-        lo_s = 0xffffffffu;
-        hi_s = 0u;
-    }
-#pragma unroll
-    for (int i = 0; i < kBucketsPer; ++i) hist[t * kBucketsPer + i] = 0;
-    if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
-    // the list stays in registers: entry q = t + kSortThreads * i
-    int32_t id[kSortPer];
-    uint32_t zb[kSortPer];   // order bits of zmin
-    uint32_t mylo = 0xffffffffu, myhi = 0u;
-#pragma unroll
-    for (int i = 0; i < kSortPer; ++i) {
-        const int q = t + kSortThreads * i;
-        id[i] = 0;
-        zb[i] = 0;
-        if (q < cnt) {
-            id[i] = entries[o + q];
-            zb[i] = float_order_bits(__uint_as_float(fbin[id[i]].zmin_bits));
-            mylo = min(mylo, zb[i]);
-            myhi = max(myhi, zb[i]);
-        }
-    }
-    __syncthreads();
-    atomicMin(&lo_s, mylo);
-    atomicMax(&hi_s, myhi);
-    __syncthreads();
-    const float lo = order_bits_float(lo_s), hi = order_bits_float(hi_s);
-    const float scale = (hi > lo) ? (float)kSortBuckets / (hi - lo) : 0.0f;
-    int bk[kSortPer];
-#pragma unroll
-    for (int i = 0; i < kSortPer; ++i) {
-        int k = (int)((order_bits_float(zb[i]) - lo) * scale);
-        k = k < 0 ? 0 : (k >= kSortBuckets ? kSortBuckets - 1 : k);
-        bk[i] = k;
-        if (t + kSortThreads * i < cnt) atomicAdd(&hist[k], 1);
-    }
-    __syncthreads();
-    // bucket starts: each thread owns kBucketsPer consecutive buckets
-    {
-        int c[kBucketsPer];
-        int local = 0;
-#pragma unroll
-        for (int i = 0; i < kBucketsPer; ++i) {
-            c[i] = hist[t * kBucketsPer + i];
-            local += c[i];
-        }
-        int run = block256_exclusive_sum(local, wsum);
-#pragma unroll
-        for (int i = 0; i < kBucketsPer; ++i) {
-            hist[t * kBucketsPer + i] = run;
-            run += c[i];
-        }
-    }
-    __syncthreads();
-    // Every entry has been read: scatter the ids to their sorted places in
-    // the list, and note each round's smallest depth bound.
-#pragma unroll
-    for (int i = 0; i < kSortPer; ++i) {
-        if (t + kSortThreads * i < cnt) {
-            const int pos = atomicAdd(&hist[bk[i]], 1);
-            entries[o + pos] = id[i];
-            atomicMin(&rmin[pos / kFineThreads], zb[i]);
-        }
-    }
-    __syncthreads();
-    if (t == 0) {
-        uint32_t run = 0xffffffffu;
-        for (int r = kRoundsPerBin - 1; r >= 0; --r) {
-            run = min(run, rmin[r]);
-            lb[r] = (run == 0xffffffffu) ? __builtin_inff() : order_bits_float(run);
-        }
-    }
+    // short lists (the common case) take a variant with fewer registers and
+    // buckets
+    if (cnt <= 2 * kSortThreads)
+        sort_list<2, kSortThreads>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
+    else if (cnt <= 4 * kSortThreads)
+        sort_list<4, kSortBuckets>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
+    else
+        sort_list<kSortPer, kSortBuckets>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
 }
 
 // ---------------------------------------------------------------------------
