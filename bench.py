@@ -173,15 +173,23 @@ def measured_traffic(kernel: str, workload: str):
 
 
 def copy_calibration(nbytes: int, reps: int) -> None:
-    """A plain device copy of a known size, for calibrating the HBM byte
-    counters (run under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE)."""
+    """Kernels of known traffic, for calibrating the HBM byte counters (run
+    under rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE): a plain device copy
+    (reads and writes nbytes), a sum (reads nbytes, 16-byte loads) and a
+    fill (writes nbytes). Two kernels that read the same bytes with
+    different request patterns check that one scale fits both."""
     import torch
 
     dev = torch.device("cuda:0")
     src = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
+    acc = torch.empty((), dtype=torch.float32, device=dev)
     for _ in range(reps):
         dst.copy_(src)
+    for _ in range(reps):
+        torch.sum(src, dim=0, out=acc)
+    for _ in range(reps):
+        dst.fill_(2.0)
     torch.cuda.synchronize()
     print(json.dumps({"copy_bytes": src.numel() * 4, "reps": reps}), flush=True)
 
