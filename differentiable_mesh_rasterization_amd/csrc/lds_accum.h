@@ -3,11 +3,15 @@
 // ids: an open-addressing table of 64-bit fixed-point sums, flushed with one
 // float atomic per (id, coordinate).
 //
-// Each entry's fixed-point scale is relative, not absolute: it is set by the
-// first contribution that inserts the entry (the power of two just above the
-// largest magnitude of its three coordinates) and stored in the key word next
+// Each entry's fixed-point scale is relative, not absolute: it is set when
+// the entry is inserted, to the power of two just above the largest partial
+// of the slot that inserts it (for a face's slot, the largest of its nine
+// partials, shared by its three vertices), and stored in the key word next
 // to the id, so the accuracy of the sums does not depend on the scale of the
-// upstream gradients.
+// upstream gradients. A vertex's own partial in a slot can be far smaller
+// than the slot's others (with perspective correction, a vertex whose
+// barycentric is near 0); a scale taken from it alone would push the
+// vertex's later, ordinary contributions out of the entry's range.
 #pragma once
 
 #include "dmr_internal.h"
@@ -28,16 +32,16 @@ constexpr uint32_t kIdMask = (1u << kIdBits) - 1u;
 constexpr uint32_t kEmptyKey = 0xffffffffu;
 constexpr int64_t kTableMaxId = (int64_t)kIdMask - 1;
 
-// Fixed point relative to an entry exponent e (every coordinate of the
-// entry's first contribution is below 2^e in magnitude): a contribution is
+// Fixed point relative to an entry exponent e (every partial of the slot
+// that inserted the entry is below 2^e in magnitude): a contribution is
 // rounded to a multiple of 2^(e - kFixFrac) and taken into the entry only if
 // its coordinates are below 2^(e + kFixAhead); larger ones go straight to
 // global float atomics. A tile adds at most 2^14 contributions to one entry
 // (256 pixels x 64 slots), so a sum stays below 2^(14 + kFixAhead +
-// kFixFrac) = 2^62 units. The quantum is 2^-34 relative to the first
-// contribution, far below binary32 resolution.
-constexpr int kFixFrac = 34;
-constexpr int kFixAhead = 14;
+// kFixFrac) = 2^62 units. The quantum is 2^-30 relative to the inserting
+// slot's largest partial, far below binary32 resolution.
+constexpr int kFixFrac = 30;
+constexpr int kFixAhead = 18;
 static_assert(14 + kFixFrac + kFixAhead <= 62, "64-bit fixed-point headroom");
 
 // Exponent code of a magnitude m (finite, > 0): the biased binary32 exponent
@@ -68,9 +72,9 @@ __device__ __forceinline__ float from_fixed(unsigned long long x, uint32_t code)
     return (float)((double)(long long)x * pow2d((int)code - 126 - kFixFrac));
 }
 
-// Finds or inserts the entry of `id` for a contribution of exponent code
-// `code` (1..254); returns its slot and the entry's code, or -1 when the
-// probe sequence finds no room. `first` is the result of the first probe's
+// Finds or inserts the entry of `id`, a new entry with exponent code `code`
+// (1..254); returns its slot and the entry's code, or -1 when the probe
+// sequence finds no room. `first` is the result of the first probe's
 // compare-and-swap at slot h0 (issued by the caller).
 template <int HB>
 __device__ __forceinline__ int table_find(uint32_t* hkey, uint32_t id, uint32_t code, uint32_t h0, uint32_t first,
@@ -142,13 +146,15 @@ __device__ __forceinline__ void vertex_add(uint32_t* hkey, unsigned long long (*
 // The three vertices of one face at once: the first probe of all three is
 // issued before any result is waited for, further probes (rare) follow in a
 // loop, then the nine fixed-point adds (or global float atomics for a
-// vertex the table cannot take).
+// vertex the table cannot take). New entries take the slot's scale: the
+// largest exponent code among the three vertices that go to the table.
 template <int HB = kHashBits>
 __device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (*hval)[3],
                                             float* __restrict__ grad_verts, const int64_t (&vi)[3],
                                             const float (&g)[9], bool use_hash, int run_bits) {
     uint32_t code[3], h[3], cur[3];
     bool elig[3], zero[3];
+    uint32_t slot_code = 0;
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         const float gx = g[3 * k], gy = g[3 * k + 1], gz = g[3 * k + 2];
@@ -157,16 +163,20 @@ __device__ __forceinline__ void vertex_add3(uint32_t* hkey, unsigned long long (
         code[k] = mag_code(m);
         zero[k] = code[k] == 0u && !nan;   // three zeros: nothing to add
         elig[k] = use_hash && !zero[k] && m <= 3.402823466e38f && !nan;
+        slot_code = elig[k] ? max(slot_code, code[k]) : slot_code;
+    }
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
         const uint32_t id = (uint32_t)vi[k];
         h[k] = hash_slot0(id, HB, run_bits);
-        cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], kEmptyKey, id | (code[k] << kIdBits)) : 0u;
+        cur[k] = elig[k] ? atomicCAS(&hkey[h[k]], kEmptyKey, id | (slot_code << kIdBits)) : 0u;
     }
 #pragma unroll
     for (int k = 0; k < 3; ++k) {
         if (zero[k]) continue;
         int slot = -1;
         uint32_t ec = 0;
-        if (elig[k]) slot = table_find<HB>(hkey, (uint32_t)vi[k], code[k], h[k], cur[k], ec);
+        if (elig[k]) slot = table_find<HB>(hkey, (uint32_t)vi[k], slot_code, h[k], cur[k], ec);
         if (slot >= 0 && code[k] <= ec + kFixAhead) {
             atomicAdd(&hval[slot][0], to_fixed(g[3 * k], ec));
             atomicAdd(&hval[slot][1], to_fixed(g[3 * k + 1], ec));
