@@ -803,6 +803,8 @@ struct OwnerRec {
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
 constexpr int kPairWin = 1536;
+constexpr int kLaneMinPairs = 24;    // a dense round: at least kLaneMinOwners owners
+constexpr int kLaneMinOwners = 240;  // with at least kLaneMinPairs candidate pairs each
 
 template <int KMAX, bool PERSP>
 __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KMAX <= 10 ? 4 : 1, 8))) void fine_raster(
@@ -881,6 +883,19 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
         bool done = !valid;
 
+        // The next round's list entry is loaded once this round's records
+        // are staged, and its box at the round's end, so that a round waits
+        // on its record loads only (the first round loads all three).
+        int64_t nfid = -1;
+        FaceBin nfb;
+        nfb.box_lo = 0x7fff7fff;
+        nfb.box_hi = 0;
+        nfb.mesh = 0;
+        nfb.zmin_bits = 0;
+        if (t < total) {
+            nfid = list_mode ? (int64_t)entries[o + t] : f0 + t;
+            nfb = fbin[nfid];
+        }
         for (int64_t base = 0; base < total; base += kFineThreads) {
             // pruning bound: this owner's last key, or the quad's smallest
             double bound = quarter ? quad_min(key[KMAX - 1]) : key[KMAX - 1];
@@ -892,15 +907,14 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 if (zl > __uint_as_float((uint32_t)(key_bits(bound) >> 32))) done = true;
             }
             if (__syncthreads_count(!done) == 0) break;
-            const int64_t q = base + t;
             bool live = false;
             int c0 = 0, c1 = -1, r0 = 0, r1 = -1;
-            if (q < total) {
+            const int64_t fid = nfid;
+            if (fid >= 0) {
                 // the face's pixel box, clipped to the item's region (empty
                 // for a face that is never a candidate); only faces that
                 // reach the region have their full record staged
-                const int64_t fid = list_mode ? (int64_t)entries[o + q] : f0 + q;
-                const FaceBin fb = fbin[fid];
+                const FaceBin fb = nfb;
                 c0 = max((fb.box_lo & 0xffff) - bx * kBin, reg_c);
                 c1 = min((fb.box_hi & 0xffff) - bx * kBin, reg_c + reg_w - 1);
                 r0 = max((fb.box_lo >> 16) - by * kBin, reg_r);
@@ -913,6 +927,9 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                     sface[t] = (int32_t)fid;
                 }
             }
+            const int64_t qn = base + kFineThreads + t;
+            nfid = -1;
+            if (qn < total) nfid = list_mode ? (int64_t)entries[o + qn] : f0 + qn;
             // the face's columns and rows as bit sets; ballot c of them is
             // the wave's mask for bin column (row) c (every lane writes the
             // same value)
@@ -946,6 +963,25 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             // pairs. One prefix sum per window gives the positions (low 16
             // bits) and counts the owners left for the next window (high
             // bits).
+            // A dense round of a long list (nearly every owner with many
+            // pairs) is evaluated by per-owner loops instead: the lanes of a
+            // wave then have similar trip counts, and each pair is tested
+            // against its owner's current bound, which prunes more where a
+            // push costs two instructions per list slot.
+            if (KMAX >= 16 && __syncthreads_count(left >= kLaneMinPairs) >= kLaneMinOwners) {
+                const uint64_t mw[4] = {m0, m1, m2, m3};
+#pragma unroll 1
+                for (int w = 0; w < 4; ++w) {
+#pragma unroll 1
+                    for (uint64_t x = mw[w]; x; x &= x - 1) {
+                        const uint32_t u = (uint32_t)(ubase + 64 * w + __builtin_ctzll(x));
+                        const double kk =
+                            pair_key<PERSP>(staged_rec(srec4, u), sface[u], px, py, blur, key[KMAX - 1]);
+                        if (kk < key[KMAX - 1]) topk_push<KMAX>(key, kk);
+                    }
+                }
+                left = 0;
+            }
             int active = __syncthreads_count(left > 0);
             while (active > 0) {
                 const int cap = kPairWin / active;
@@ -984,6 +1020,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                 bound = quarter ? quad_min(key[KMAX - 1]) : key[KMAX - 1];
                 orec[t].bound = bound;
             }
+            if (nfid >= 0) nfb = fbin[nfid];
             __syncthreads();
         }
         __syncthreads();
