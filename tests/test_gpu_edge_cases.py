@@ -3,7 +3,7 @@ beyond the candidate count, culled and degenerate faces, exact depth ties,
 pixel centres on shared edges, thin and one-pixel images, K = 1 and K = 64,
 a blur radius covering the image, off-screen faces, one face over every bin,
 thousands of faces in one bin, heavy bins split into quarter items, hundreds
-of faces each covering every pixel (whole and split bins), subnormal depths,
+of faces each covering every pixel (whole and split bins, K up to 64), subnormal depths,
 faces using another mesh's vertices, the largest image side, hundreds of
 small meshes, near-degenerate slivers (tiny non-zero doubled area), faces
 whose arithmetic meets NaN or overflow, invalid vertex indices, and the
@@ -206,6 +206,28 @@ def all_faces_cover_a_split_bin():
     # each with 64 candidates per round
     v, f = _covering(21, 2400)
     return v, f, [0, 2400], 16, 16, 10, 1e-4
+
+
+@case
+def all_faces_cover_every_pixel_k32():
+    # dense rounds of a long list with K = 32: every owner has 256 candidate
+    # pairs per round, so the rounds go to per-owner loops
+    v, f = _covering(23, 500)
+    return v, f, [0, 500], 24, 40, 32, 1e-3
+
+
+@case
+def all_faces_cover_every_pixel_k64():
+    v, f = _covering(24, 400)
+    return v, f, [0, 400], 20, 20, 64, 1e-3
+
+
+@case
+def all_faces_cover_a_split_bin_k16():
+    # quarter items whose four owners per pixel each have 64 candidates per
+    # round: dense rounds in per-owner loops on the quarter's own face word
+    v, f = _covering(25, 2400)
+    return v, f, [0, 2400], 16, 16, 16, 1e-4
 
 
 @case
