@@ -179,7 +179,10 @@ dmr_status rasterize_meshes_fwd_noalloc(const float* verts, int64_t V, const int
  *              not checked, and any other content gives wrong gradients. The
  *              call only reads the workspace. Without that bit the workspace
  *              is not used and may be NULL.
- * Contributions are summed per 16x16 tile and vertex in LDS, then added to
+ * Contributions are summed per 16x16 tile and vertex in LDS, in 64-bit fixed
+ * point relative to each sum's own scale (units of 2^-30 of the largest
+ * partial of the slot that started it), so the accuracy does not depend on
+ * the scale of the upstream gradients; the tile sums are then added to
  * grad_verts with float32 atomics, so the rounding of grad_verts may differ
  * between runs.
  */
