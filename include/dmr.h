@@ -3,6 +3,7 @@
  *
  * Entry points: the rasterizer's forward and backward passes
  * (rasterize_meshes_fwd, rasterize_meshes_fwd_ex with settings,
+ * rasterize_meshes_fwd_noalloc for callers that cannot allocate,
  * rasterize_meshes_bwd) and their workspace helpers; the second stage that
  * fuses each pixel's K faces (dmr_blend_fwd / dmr_blend_bwd); point clouds
  * (rasterize_points_fwd / rasterize_points_bwd); the upstream projection
