@@ -196,3 +196,23 @@ def oracle_region(oracle, verts, faces, offsets, n, H, W, K, blur, i0, i1, j0, j
         gz, gb, gd = grads
         gv = oracle.backward(verts, sub, sub_off, H, W, K, blur, p2f, gz, gb, gd, pixels=local)
     return n * H * W + local, (glob, zb, ba, ds), gv
+
+
+def point_oracle_band(rasterize_points, w, n, r0, r1, pts_np):
+    """The oracle on rows [r0, r1) of image n, run on only the points of that
+    image whose y lies within the radius (with margin) of the band's pixel
+    centres, in their original order, so that ties by index order the same;
+    the indices are mapped back to global ones. A point farther than the
+    radius from every centre of the band is never a candidate there, so
+    this equals the whole-image oracle on the band."""
+    lo, hi = int(w.offsets[n]), int(w.offsets[n + 1])
+    q = pts_np[lo:hi]
+    yc = (np.arange(r0, r1, dtype=np.float64) * 2 + 1) / w.H - 1
+    pad = 2.0 * w.radius + 1e-6
+    keep = np.nonzero((q[:, 1] >= yc.min() - pad) & (q[:, 1] <= yc.max() + pad))[0]
+    pix = (np.arange(r0, r1)[:, None] * w.W + np.arange(w.W)[None, :]).reshape(-1)
+    idx, zb, ds = rasterize_points(q[keep], [0, len(keep)], w.H, w.W, w.K, w.radius, pixels=pix)
+    gidx = np.full_like(idx, -1)
+    if len(keep):
+        gidx = np.where(idx >= 0, lo + keep[np.maximum(idx, 0)], -1)
+    return gidx, zb, ds

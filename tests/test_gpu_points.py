@@ -9,7 +9,7 @@ import torch
 
 from gpu_util import DEV, require_gpu, say, to_dev
 from oracle.points import rasterize_points, rasterize_points_backward
-from parity import rel_l2
+from parity import point_oracle_band, rel_l2
 from workloads import make_point_workload, point_upstream_grads
 
 pytestmark = pytest.mark.gpu
@@ -93,6 +93,28 @@ def test_points_full_size_sampled(dmr):
     refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, ref[0], g["zbuf"].reshape(-1, w.K)[pix],
                                      g["dists"].reshape(-1, w.K)[pix], pixels=pix)
     assert rel_l2(gp.cpu().numpy(), refg) <= 1e-5
+
+
+def test_points_full_size_dense_largest_cloud(dmr):
+    """points16_256 in the bench's launch configuration: every pixel of the
+    image of its largest cloud, bit for bit against the oracle (16 bands of
+    16 rows)."""
+    w = make_point_workload("points16_256")
+    n = int(np.argmax(np.diff(w.offsets)))
+    say(f"[gpu] points dense whole image {n} of points16_256 ({int(np.diff(w.offsets)[n])} points)")
+    out, _, _ = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    got = [t[n].cpu().numpy().reshape(w.H * w.W, w.K) for t in out]
+    pts_np = np.asarray(w.points, np.float32).reshape(-1, 3)
+    filled = 0
+    for r0 in range(0, w.H, 16):
+        r1 = min(w.H, r0 + 16)
+        ref = point_oracle_band(rasterize_points, w, n, r0, r1, pts_np)
+        rows = slice(r0 * w.W, r1 * w.W)
+        for g, r in zip(got, ref):
+            np.testing.assert_array_equal(g[rows], r)
+        filled += int((ref[0] >= 0).sum())
+    say(f"  {filled} filled slots, all equal")
+    assert filled > 0
 
 
 def test_points_small_workspace_is_exact(dmr):

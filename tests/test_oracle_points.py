@@ -128,3 +128,22 @@ def test_backward_matches_finite_differences(seed):
             assert grad[q, c] == pytest.approx((Lp - Lm) / (2 * h), rel=1e-6, abs=1e-7)
             tested += 1
     assert tested >= 30
+
+
+@pytest.mark.parametrize("name", ["points_small", "points_soup"])
+def test_point_band_oracle_equals_whole_oracle(name):
+    """The band reduction the dense full-size GPU check uses
+    (parity.point_oracle_band: the oracle on one image's points near a band
+    of 16 rows, indices mapped back) gives exactly the whole-batch oracle on
+    every pixel of every image."""
+    from parity import point_oracle_band
+
+    w = make_point_workload(name)
+    pts = np.asarray(w.points, np.float32).reshape(-1, 3)
+    full = rasterize_points(w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    for n in range(len(w.offsets) - 1):
+        for r0 in range(0, w.H, 16):
+            r1 = min(w.H, r0 + 16)
+            band = point_oracle_band(rasterize_points, w, n, r0, r1, pts)
+            for a, b in zip(band, full):
+                np.testing.assert_array_equal(a, b[n].reshape(w.H * w.W, w.K)[r0 * w.W:r1 * w.W])
