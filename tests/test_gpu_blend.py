@@ -112,6 +112,30 @@ def test_blend_full_size_sampled(dmr, name, n):
     _check(ref, sel(rgba, (4,)), (rz, rd), (sel(gz, (K,)), sel(gd, (K,))), sc)
 
 
+def test_blend_full_size_dense(dmr):
+    # every pixel of every image of hetero16_256 (16 x 256 x 256 x 10 slots),
+    # and every pixel of the soups32_512 image with the largest soup
+    # (512 x 512 x 50 slots), each blended at full size in one launch
+    prm = PARAMS["sharp"]
+    for name in ("hetero16_256", "soups32_512"):
+        w = make_workload(name)
+        say(f"[gpu] blend {name} dense")
+        g = GpuCase.from_workload(w)
+        p2f, zbuf, _, dists = g.forward()
+        colors = face_colors(w)
+        grad = blend_upstream_grads(w)
+        rgba, gz, gd = _blend_gpu(dmr, p2f, zbuf, dists, to_dev(colors), prm, to_dev(grad))
+        imgs = range(w.N) if name == "hetero16_256" else [int(np.diff(w.offsets).argmax())]
+        for n in imgs:
+            hp, hz, hd = p2f[n].cpu().numpy(), zbuf[n].cpu().numpy(), dists[n].cpu().numpy()
+            gs = grad[n]
+            ref = blend_forward(hp, hz, hd, colors, prm)
+            rz, rd = blend_backward(hp, hz, hd, colors, prm, gs)
+            sc = blend_backward_scale(hp, hz, hd, colors, prm, gs)
+            _check(ref, rgba[n].cpu().numpy(), (rz, rd), (gz[n].cpu().numpy(), gd[n].cpu().numpy()), sc)
+            assert (hp >= 0).any()
+
+
 @pytest.mark.parametrize("K", [1, 20, 64])
 def test_blend_edge_slots(dmr, K):
     # empty pixels, out-of-range face indices (empty slots), ties; K = 20 and
