@@ -133,3 +133,31 @@ def test_backward_error_bound_holds_for_float32_evaluation():
     assert (np.abs(gc - rgm) <= bm + 1e-30).all()
     # and it is not vacuous: a relative error of 1e-4 on one entry breaks it
     assert not (np.abs(gv * (1 + 1e-4) - rgx) <= bv).all()
+
+
+def test_error_bounds_hand_cases():
+    # The bounds written out by hand for one vertex X = (1, 1, 1), with
+    # u = 2^-24 and g4 = 4u / (1 - 4u) (four rounded products summed).
+    u = 2.0 ** -24
+    g4 = 4 * u / (1 - 4 * u)
+    X = np.array([[1.0, 1.0, 1.0]])
+    # identity camera: h = (1, 1, 1, 1), every |M||X| row sum is 1, so each
+    # h_r is off by g4; x = h0 / h3 takes both operands' errors and one
+    # rounding of the quotient; z = h2 only its own
+    b = project_forward_error_bound(X, [0, 1], np.eye(4)[None])
+    np.testing.assert_allclose(b, [[2 * g4 + u, 2 * g4 + u, g4]], rtol=1e-12, atol=0)
+    # h3 = 2 (M33 = 2): x = 1/2, off by (g4 + (1/2) 2 g4) / 2 + u / 2
+    M2 = np.diag([1.0, 1.0, 1.0, 2.0])[None]
+    b = project_forward_error_bound(X, [0, 1], M2)
+    np.testing.assert_allclose(b, [[g4 + u / 2, g4 + u / 2, g4]], rtol=1e-12, atol=0)
+    # backward with g = (1, 1, 1) through the identity: gh = (1, 1, 1, 2);
+    # the errors of gh: g eh3 / h3^2 + u gh for the first two, 0 for the
+    # third, (g0 e_x + g1 e_y) / h3 + gh3 (eh3 / h3 + 4u) for the fourth
+    bv, bm = project_backward_error_bound(X, [0, 1], np.eye(4)[None], np.ones((1, 3)))
+    dgh = np.array([g4 + u, g4 + u, 0.0, 2 * (2 * g4 + u) + 2 * (g4 + 4 * u)])
+    gh = np.array([1.0, 1.0, 1.0, 2.0])
+    # vertex entry c: sum_r |M_rc| (dgh_r + g4 gh_r), doubled
+    np.testing.assert_allclose(bv, 2 * (dgh[:3] + g4 * gh[:3])[None], rtol=1e-12, atol=0)
+    # camera entry (r, c): (dgh_r + u gh_r) |Xh_c| plus one addition (a mesh
+    # of one vertex) of u gh_r |Xh_c|, doubled
+    np.testing.assert_allclose(bm[0], 2 * np.repeat((dgh + 2 * u * gh)[:, None], 4, axis=1), rtol=1e-12, atol=0)
