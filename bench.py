@@ -15,7 +15,8 @@ Prints one JSON line:
                         HIP events on the stream it runs on inside the timed
                         region;
   valu                  the step's algorithmic fp32 flops against the fp32
-                        vector peak;
+                        vector peak (packed, and the unpacked peak the
+                        kernels can reach without packed instructions);
   configs               every workload of the benchmark suite (a 64x64
                         sphere, 8 spheres at 137x137, the headline batch, a
                         1M-triangle soup at 1024x1024, 32 soups at 512x512
@@ -40,6 +41,9 @@ import time
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 VALU_PEAK_TFLOPS = 157.3     # MI355X fp32 vector (packed), TFLOP/s
+# The kernels are built without packed fp32 instructions, so one lane
+# retires one fp32 operation per instruction: half the packed peak.
+VALU_UNPACKED_TFLOPS = 78.6
 
 METRIC = "forward+backward Mpixels*K/s at 1 MI355X; % of fp32-VALU/HBM roofline"
 SUITE = ("sphere64", "spheres8_137", "hetero16_256", "soup1m_1024", "soups32_512")
@@ -282,7 +286,8 @@ def kernel_breakdown(dmr, torch, fn, steps: int):
 def fractions(nbytes, flops, ms):
     s = ms * 1e-3
     return {"hbm_frac": round(nbytes / s / 1e9 / HBM_PEAK_GBS, 4),
-            "valu_frac": round(flops / s / 1e12 / VALU_PEAK_TFLOPS, 5)}
+            "valu_frac": round(flops / s / 1e12 / VALU_PEAK_TFLOPS, 5),
+            "valu_frac_unpacked": round(flops / s / 1e12 / VALU_UNPACKED_TFLOPS, 5)}
 
 
 def measure_config(dmr, torch, w, dev, steps: int, warmup: int):
@@ -696,6 +701,8 @@ def main():
         "valu": {"bound": "valu", "achieved": round((fl["fwd"] + fl["bwd"]) / step_s / 1e12, 3),
                  "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                  "frac": round((fl["fwd"] + fl["bwd"]) / step_s / 1e12 / VALU_PEAK_TFLOPS, 5),
+                 "peak_unpacked": VALU_UNPACKED_TFLOPS,
+                 "frac_unpacked": round((fl["fwd"] + fl["bwd"]) / step_s / 1e12 / VALU_UNPACKED_TFLOPS, 5),
                  "flops_per_step": fl["fwd"] + fl["bwd"], "P_bbox": p_bbox, "P_acc_est": p_acc},
         "kernels": kernels,
         "fwd_bwd_hbm_frac": round((nb["fwd_total"] + nb["bwd_total"]) / step_s / 1e9 / HBM_PEAK_GBS, 4),
