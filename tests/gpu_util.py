@@ -7,6 +7,9 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
+from parity import assert_forward_parity, compare_forward, oracle_excuse, oracle_region, rel_l2
+
 DEV = torch.device("cuda:0")
 
 
@@ -99,3 +102,48 @@ def rows(out, pixel_ids, K):
 
 def say(*a):
     print(*a, flush=True)
+
+
+def dense_region_check(w, g, out, n, bands, settings=0):
+    """Every pixel of the given row bands [(i0, i1)] of image n, full width:
+    the forward outputs against the oracle, and the backward pass with N(0,1)
+    upstream gradients on those pixels only (zero elsewhere) against the
+    oracle's sum over them. The oracle runs band by band on the faces that
+    can reach the band (parity.oracle_region), under the rasterizer settings
+    `settings`: those `out` was computed with (g.backward applies the
+    settings of g's last forward call)."""
+    rng = np.random.Generator(np.random.PCG64(4242 + n))
+    shape = (w.N, w.H, w.W, w.K)
+    dense = {k: (torch.zeros(shape + ((3,) if k == "bary" else ()), dtype=torch.float32, device=DEV)
+                 if k in w.grads else None) for k in ("zbuf", "bary", "dists")}
+    reports, ref_gv = [], np.zeros((w.V, 3))
+    for i0, i1 in bands:
+        npx = (i1 - i0) * w.W
+        gr = {k: (rng.standard_normal((npx, w.K) + ((3,) if k == "bary" else ()), dtype=np.float32)
+                  if k in w.grads else None) for k in ("zbuf", "bary", "dists")}
+        pix, ref, gv = oracle_region(oracle, w.verts, w.faces, w.offsets, n, w.H, w.W, w.K, w.blur, i0, i1, 0, w.W,
+                                     grads=(gr["zbuf"], gr["bary"], gr["dists"]), settings=settings)
+        ref_gv += gv
+        got = rows(out, pix, w.K)
+        reports.append(compare_forward(ref, got, w.K, excuse=oracle_excuse(oracle, w.verts, w.faces, w.offsets, w.H,
+                                                                           w.W, w.blur, pixel_ids=pix,
+                                                                           settings=settings)))
+        for k, t in dense.items():
+            if t is not None:
+                t[n, i0:i1] = to_dev(gr[k].reshape((i1 - i0, w.W, w.K) + t.shape[4:]))
+    rep = {"pixels": sum(r["pixels"] for r in reports),
+           "excused": sum((r["excused"] for r in reports), []), "unexcused": sum((r["unexcused"] for r in reports), []),
+           "max_err_zbuf": max(r["max_err_zbuf"] for r in reports),
+           "max_err_bary": max(r["max_err_bary"] for r in reports),
+           "max_err_dists": max(r["max_err_dists"] for r in reports),
+           "padding_ok": all(r["padding_ok"] for r in reports), "values_ok": all(r["values_ok"] for r in reports),
+           "filled_slots": sum(r["filled_slots"] for r in reports)}
+    say(f"  {rep['pixels']} pixels, filled={rep['filled_slots']} excused={len(rep['excused'])} "
+        f"err z/b/d={rep['max_err_zbuf']:.2e}/{rep['max_err_bary']:.2e}/{rep['max_err_dists']:.2e}")
+    assert rep["filled_slots"] > 0
+    assert_forward_parity(rep, max_excused_frac=1e-4)
+    gv = g.backward(out[0], dense["zbuf"], dense["bary"], dense["dists"]).cpu().numpy()
+    err, err_z = rel_l2(gv, ref_gv), rel_l2(gv[:, 2], ref_gv[:, 2])
+    say(f"  backward rel L2 = {err:.2e}, depth coordinates {err_z:.2e}")
+    assert np.linalg.norm(ref_gv) > 0
+    assert err <= 1e-4 and err_z <= 1e-4

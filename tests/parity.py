@@ -174,7 +174,7 @@ def region_faces(verts, faces, offsets, n, H, W, blur, i0, i1, j0, j1, margin=1e
     return f0 + np.nonzero(keep)[0]
 
 
-def oracle_region(oracle, verts, faces, offsets, n, H, W, K, blur, i0, i1, j0, j1, grads=None):
+def oracle_region(oracle, verts, faces, offsets, n, H, W, K, blur, i0, i1, j0, j1, grads=None, settings=0):
     """The oracle on the pixels of rows [i0, i1) x columns [j0, j1) of image
     n, run on the faces that can reach them (region_faces): the kept faces
     form one mesh in their global order, so depth ties break as in the
@@ -183,18 +183,21 @@ def oracle_region(oracle, verts, faces, offsets, n, H, W, K, blur, i0, i1, j0, j
     Returns (flat global pixel ids in row-major order, (pix_to_face, zbuf,
     bary, dists) for those pixels, and, with grads = (gz, gb, gd) shaped
     like the outputs (or None each), the oracle's grad_verts [V, 3] over
-    them)."""
+    them). `settings` (the oracle's setting bits) applies to both passes:
+    culling and perspective correction only remove or reweight candidates
+    that the region's box test already bounds, so the reduction holds under
+    every setting."""
     kept = region_faces(verts, faces, offsets, n, H, W, blur, i0, i1, j0, j1)
     sub = np.ascontiguousarray(np.asarray(faces, np.int64)[kept])
     ii, jj = np.meshgrid(np.arange(i0, i1), np.arange(j0, j1), indexing="ij")
     local = (ii * W + jj).reshape(-1).astype(np.int64)
     sub_off = np.array([0, len(kept)], np.int64)
-    p2f, zb, ba, ds = oracle.rasterize(verts, sub, sub_off, H, W, K, blur, pixels=local)
+    p2f, zb, ba, ds = oracle.rasterize(verts, sub, sub_off, H, W, K, blur, pixels=local, settings=settings)
     glob = np.append(kept, -1)[np.where(p2f >= 0, p2f, len(kept))]
     gv = None
     if grads is not None:
         gz, gb, gd = grads
-        gv = oracle.backward(verts, sub, sub_off, H, W, K, blur, p2f, gz, gb, gd, pixels=local)
+        gv = oracle.backward(verts, sub, sub_off, H, W, K, blur, p2f, gz, gb, gd, pixels=local, settings=settings)
     return n * H * W + local, (glob, zb, ba, ds), gv
 
 

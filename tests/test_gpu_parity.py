@@ -17,8 +17,8 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, GpuCase, host, require_gpu, rows, say, to_dev
-from parity import assert_forward_parity, compare_forward, oracle_excuse, oracle_region, rel_l2
+from gpu_util import DEV, GpuCase, dense_region_check, host, require_gpu, rows, say, to_dev
+from parity import assert_forward_parity, compare_forward, oracle_excuse, rel_l2
 from workloads import make_workload, masked_upstream_grads, sample_pixels, upstream_grads
 
 pytestmark = pytest.mark.gpu
@@ -150,48 +150,6 @@ def test_backward_full_size_sampled(dmr, name):
     assert err <= 1e-4
 
 
-def _dense_region_check(w, g, out, n, bands):
-    """Every pixel of the given row bands [(i0, i1)] of image n, full width:
-    the forward outputs against the oracle, and the backward pass with N(0,1)
-    upstream gradients on those pixels only (zero elsewhere) against the
-    oracle's sum over them. The oracle runs band by band on the faces that
-    can reach the band (parity.oracle_region)."""
-    rng = np.random.Generator(np.random.PCG64(4242 + n))
-    shape = (w.N, w.H, w.W, w.K)
-    dense = {k: (torch.zeros(shape + ((3,) if k == "bary" else ()), dtype=torch.float32, device=DEV)
-                 if k in w.grads else None) for k in ("zbuf", "bary", "dists")}
-    reports, ref_gv = [], np.zeros((w.V, 3))
-    for i0, i1 in bands:
-        npx = (i1 - i0) * w.W
-        gr = {k: (rng.standard_normal((npx, w.K) + ((3,) if k == "bary" else ()), dtype=np.float32)
-                  if k in w.grads else None) for k in ("zbuf", "bary", "dists")}
-        pix, ref, gv = oracle_region(oracle, w.verts, w.faces, w.offsets, n, w.H, w.W, w.K, w.blur, i0, i1, 0, w.W,
-                                     grads=(gr["zbuf"], gr["bary"], gr["dists"]))
-        ref_gv += gv
-        got = rows(out, pix, w.K)
-        reports.append(compare_forward(ref, got, w.K, excuse=oracle_excuse(oracle, w.verts, w.faces, w.offsets, w.H,
-                                                                           w.W, w.blur, pixel_ids=pix)))
-        for k, t in dense.items():
-            if t is not None:
-                t[n, i0:i1] = to_dev(gr[k].reshape((i1 - i0, w.W, w.K) + t.shape[4:]))
-    rep = {"pixels": sum(r["pixels"] for r in reports),
-           "excused": sum((r["excused"] for r in reports), []), "unexcused": sum((r["unexcused"] for r in reports), []),
-           "max_err_zbuf": max(r["max_err_zbuf"] for r in reports),
-           "max_err_bary": max(r["max_err_bary"] for r in reports),
-           "max_err_dists": max(r["max_err_dists"] for r in reports),
-           "padding_ok": all(r["padding_ok"] for r in reports), "values_ok": all(r["values_ok"] for r in reports),
-           "filled_slots": sum(r["filled_slots"] for r in reports)}
-    say(f"  {rep['pixels']} pixels, filled={rep['filled_slots']} excused={len(rep['excused'])} "
-        f"err z/b/d={rep['max_err_zbuf']:.2e}/{rep['max_err_bary']:.2e}/{rep['max_err_dists']:.2e}")
-    assert rep["filled_slots"] > 0
-    assert_forward_parity(rep, max_excused_frac=1e-4)
-    gv = g.backward(out[0], dense["zbuf"], dense["bary"], dense["dists"]).cpu().numpy()
-    err, err_z = rel_l2(gv, ref_gv), rel_l2(gv[:, 2], ref_gv[:, 2])
-    say(f"  backward rel L2 = {err:.2e}, depth coordinates {err_z:.2e}")
-    assert np.linalg.norm(ref_gv) > 0
-    assert err <= 1e-4 and err_z <= 1e-4
-
-
 def test_dense_bin_band_soup1m(dmr):
     """soup1m_1024 in the benchmark's launch configuration: every pixel of
     one 16-row bin band (16,384 pixels, 64 bins; the 1M-face soup stresses
@@ -200,7 +158,7 @@ def test_dense_bin_band_soup1m(dmr):
     say("[gpu] dense bin band of soup1m_1024: rows 512-527, all columns")
     g = GpuCase.from_workload(w)
     out = g.forward()
-    _dense_region_check(w, g, out, 0, [(512, 528)])
+    dense_region_check(w, g, out, 0, [(512, 528)])
 
 
 def test_dense_largest_mesh_soups32(dmr):
@@ -212,7 +170,7 @@ def test_dense_largest_mesh_soups32(dmr):
     say(f"[gpu] dense whole image {n} of soups32_512 ({int(np.diff(w.offsets)[n])} faces)")
     g = GpuCase.from_workload(w)
     out = g.forward()
-    _dense_region_check(w, g, out, n, [(i0, min(w.H, i0 + 16)) for i0 in range(0, w.H, 16)])
+    dense_region_check(w, g, out, n, [(i0, min(w.H, i0 + 16)) for i0 in range(0, w.H, 16)])
 
 
 def test_zbuf_gradient_identity_dense(dmr):

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_util import DEV, GpuCase, host, require_gpu, rows, say, to_dev
+from gpu_util import DEV, GpuCase, dense_region_check, host, require_gpu, rows, say, to_dev
 from parity import assert_forward_parity, compare_forward, oracle_excuse, rel_l2
 from workloads import make_workload, masked_upstream_grads, sample_pixels, upstream_grads
 
@@ -117,6 +117,20 @@ def test_settings_full_size_sampled(dmr, sname):
     err = rel_l2(gv, refg)
     say(f"  backward rel L2 = {err:.2e}")
     assert err <= 1e-4
+
+
+@pytest.mark.parametrize("sname", ["persp", "cull", "all"])
+def test_settings_dense_largest_mesh_hetero(dmr, sname):
+    """hetero16_256 in the benchmark's launch configuration under a setting:
+    every pixel of the image of its largest mesh (65,536 pixels, K = 10),
+    forward and backward, against the oracle with the same setting."""
+    settings = SETTINGS[sname]
+    w = make_workload("hetero16_256")
+    n = int(np.argmax(np.diff(w.offsets)))
+    say(f"[gpu] settings {sname}: dense whole image {n} of hetero16_256 ({int(np.diff(w.offsets)[n])} faces)")
+    g = GpuCase.from_workload(w)
+    out = g.forward(settings=settings)
+    dense_region_check(w, g, out, n, [(i0, min(w.H, i0 + 16)) for i0 in range(0, w.H, 16)], settings=settings)
 
 
 def test_autograd_wrapper_settings(dmr):
