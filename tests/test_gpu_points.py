@@ -98,14 +98,16 @@ def test_points_full_size_sampled(dmr):
 def test_points_full_size_dense_largest_cloud(dmr):
     """points16_256 in the bench's launch configuration: every pixel of the
     image of its largest cloud, bit for bit against the oracle (16 bands of
-    16 rows)."""
+    16 rows); then the backward pass with N(0,1) upstream gradients on every
+    slot of that image (zero elsewhere) against the oracle's sum."""
     w = make_point_workload("points16_256")
     n = int(np.argmax(np.diff(w.offsets)))
     say(f"[gpu] points dense whole image {n} of points16_256 ({int(np.diff(w.offsets)[n])} points)")
-    out, _, _ = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
+    out, (p, o), _ = _gpu(dmr, w.points, w.offsets, w.H, w.W, w.K, w.radius)
     got = [t[n].cpu().numpy().reshape(w.H * w.W, w.K) for t in out]
     pts_np = np.asarray(w.points, np.float32).reshape(-1, 3)
     filled = 0
+    ref_idx = []
     for r0 in range(0, w.H, 16):
         r1 = min(w.H, r0 + 16)
         ref = point_oracle_band(rasterize_points, w, n, r0, r1, pts_np)
@@ -113,8 +115,25 @@ def test_points_full_size_dense_largest_cloud(dmr):
         for g, r in zip(got, ref):
             np.testing.assert_array_equal(g[rows], r)
         filled += int((ref[0] >= 0).sum())
+        ref_idx.append(ref[0])
     say(f"  {filled} filled slots, all equal")
     assert filled > 0
+    rng = np.random.Generator(np.random.PCG64(77 + n))
+    gz = rng.standard_normal((w.H * w.W, w.K), dtype=np.float32)
+    gd = rng.standard_normal((w.H * w.W, w.K), dtype=np.float32)
+    shape = (w.N, w.H, w.W, w.K)
+    dz = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    dd = torch.zeros(shape, dtype=torch.float32, device=DEV)
+    dz[n] = to_dev(gz.reshape(w.H, w.W, w.K))
+    dd[n] = to_dev(gd.reshape(w.H, w.W, w.K))
+    gp = torch.empty_like(p)
+    dmr.rasterize_points_bwd(p, o, w.H, w.W, w.K, out[0], dz, dd, gp)
+    pix = n * w.H * w.W + np.arange(w.H * w.W, dtype=np.int64)
+    refg = rasterize_points_backward(w.points, w.offsets, w.H, w.W, w.K, np.concatenate(ref_idx), gz, gd, pixels=pix)
+    err = rel_l2(gp.cpu().numpy(), refg)
+    say(f"  backward rel L2 = {err:.2e}")
+    assert np.linalg.norm(refg) > 0
+    assert err <= 1e-5
 
 
 def test_points_small_workspace_is_exact(dmr):
