@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     const PointRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t P, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     const WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
-    int64_t capacity, int32_t H, int32_t W, int32_t K, float r2, int32_t nbx, int32_t nby,
+    int64_t capacity, int32_t sort_min, int32_t H, int32_t W, int32_t K, float r2, int32_t nbx, int32_t nby,
     int64_t* __restrict__ out_idx, float* __restrict__ zbuf, float* __restrict__ dists) {
     __shared__ PointRec spt[kPointThreads];
     __shared__ uint64_t colmask[kBin][kPointThreads / 64];
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(kPointThreads) void point_raster(
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
     const bool list_mode = o + cnt <= capacity;
-    const bool sorted = list_sorted(o, cnt, capacity);
+    const bool sorted = list_sorted(o, cnt, capacity, sort_min);
     const float* lb = round_lb + b * kRoundsPerBin;
     int64_t f0 = off[n], f1 = off[n + 1];
     f0 = f0 < 0 ? 0 : f0;
@@ -316,7 +316,8 @@ hipError_t launch_points_forward(const FwdArgs& a) {
     timing_begin(kKPointRaster, a.stream);
 #define DMR_POINTS(KM)                                                                                               \
     point_raster<KM><<<grid, kPointThreads, 0, a.stream>>>(recs, fbin, a.F, a.off, count, offset, items, hdr,       \
-                                                           entries, round_lb, a.capacity, a.H, a.W, a.K, r2,        \
+                                                           entries, round_lb, a.capacity,                           \
+                                                           sort_min_entries(a.K), a.H, a.W, a.K, r2,                \
                                                            (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face,       \
                                                            a.zbuf, a.dists)
     if (a.K <= 1) DMR_POINTS(1);

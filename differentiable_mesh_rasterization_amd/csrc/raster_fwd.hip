@@ -235,7 +235,7 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
                                                          int64_t* __restrict__ offset,
                                                          int32_t* __restrict__ rep, int32_t replicas,
                                                          int32_t* __restrict__ perm, uint32_t* __restrict__ items,
-                                                         int64_t bins, int32_t allow_split,
+                                                         int64_t bins, int32_t allow_split, int32_t sort_min,
                                                          const int32_t* __restrict__ block_live,
                                                          int64_t nblocks, int64_t capacity, size_t base_bytes,
                                                          WsHeader* __restrict__ hdr) {
@@ -301,6 +301,10 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
             item_at[t] = y - y0;
         }
         if (t == kOrderBuckets - 1) hdr->fine_items = y;
+        // every bin with more than sort_min faces lies in a bucket up to
+        // that of sort_min + 1: the sort visits the order's prefix of those
+        // buckets
+        if (t == order_bucket(sort_min + 1)) hdr->sort_bins = x;
     }
     __syncthreads();
     int64_t over = 0;
@@ -541,16 +545,19 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
                                                          const int64_t* __restrict__ offset,
                                                          const int32_t* __restrict__ perm,
                                                          int32_t* __restrict__ entries, int64_t capacity,
+                                                         int32_t sort_min, const WsHeader* __restrict__ hdr,
                                                          float* __restrict__ round_lb) {
     __shared__ int32_t hist[kSortBuckets];
     __shared__ int wsum[kSortThreads / 64];
     __shared__ uint32_t lo_s, hi_s;
     __shared__ uint32_t rmin[kRoundsPerBin];
+    // the bins past the order's prefix of sortable ones end at once
+    if ((int32_t)blockIdx.x >= hdr->sort_bins) return;
     const int64_t b = perm[blockIdx.x];
     const int32_t cnt = count[b];
     const int64_t o = offset[b];
     float* lb = round_lb + b * kRoundsPerBin;
-    if (!list_sorted(o, cnt, capacity)) return;   // the fine passes read no bound of it
+    if (!list_sorted(o, cnt, capacity, sort_min)) return;   // the fine passes read no bound of it
     // short lists (the common case) take a variant with fewer registers and
     // buckets
     if (cnt <= 2 * kSortThreads)
@@ -647,14 +654,20 @@ __device__ __forceinline__ double pair_key(const FaceRec& r, int32_t face, float
         const float invS = 1.0f / S;
         z = ((c0 * invS) * r.z0 + (c1 * invS) * r.z1) + (c2 * invS) * r.z2;
     }
-    const float d0 = edge_dist2(dx0, dy0, r.x1 - r.x0, r.y1 - r.y0, r.il0);
-    const float d1 = edge_dist2(dx1, dy1, r.x2 - r.x1, r.y2 - r.y1, r.il1);
-    const float d2 = edge_dist2(dx2, dy2, r.x0 - r.x2, r.y0 - r.y2, r.il2);
-    float d = d0;
-    d = d1 < d ? d1 : d;
-    d = d2 < d ? d2 : d;
-    // outside the triangle, d < blur fails for every blur <= 0 (d >= 0)
-    const bool cand = (inside || d < blur) && (z > 0.0f);
+    // Outside the triangle, d < blur fails for every blur <= 0 (d is a sum
+    // of squares, >= 0 or NaN), so the distances are only needed with a
+    // positive blur (a test on a kernel argument: uniform, no divergence).
+    bool near = false;
+    if (blur > 0.0f) {
+        const float d0 = edge_dist2(dx0, dy0, r.x1 - r.x0, r.y1 - r.y0, r.il0);
+        const float d1 = edge_dist2(dx1, dy1, r.x2 - r.x1, r.y2 - r.y1, r.il1);
+        const float d2 = edge_dist2(dx2, dy2, r.x0 - r.x2, r.y0 - r.y2, r.il2);
+        float d = d0;
+        d = d1 < d ? d1 : d;
+        d = d2 < d ? d2 : d;
+        near = d < blur;
+    }
+    const bool cand = (inside || near) && (z > 0.0f);
     const double kk = make_key(z, face);
     return (cand && kk < bound) ? kk : empty_key();
 }
@@ -803,6 +816,10 @@ struct OwnerRec {
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
 constexpr int kPairWin = 1536;
+// For K <= 2 the windows hold half as many pairs (measured faster on the
+// 1M-triangle soup at K = 1; a fifth workgroup per CU, which the smaller
+// LDS footprint would allow, changed nothing).
+constexpr int kPairWinSmallK = 768;
 constexpr int kLaneMinPairs = 24;    // a dense round: at least kLaneMinOwners owners
 constexpr int kLaneMinOwners = 240;  // with at least kLaneMinPairs candidate pairs each
 
@@ -811,8 +828,8 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     const FaceRec* __restrict__ recs, const FaceBin* __restrict__ fbin, int64_t F, const int64_t* __restrict__ off,
     const int32_t* __restrict__ count, const int64_t* __restrict__ offset, const uint32_t* __restrict__ items,
     WsHeader* __restrict__ hdr, const int32_t* __restrict__ entries, const float* __restrict__ round_lb,
-    int64_t capacity, int32_t H, int32_t W, int32_t K, float blur, uint32_t settings, int32_t nbx, int32_t nby,
-    int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
+    int64_t capacity, int32_t sort_min, int32_t H, int32_t W, int32_t K, float blur, uint32_t settings, int32_t nbx,
+    int32_t nby, int64_t* __restrict__ pix_to_face, float* __restrict__ zbuf, float* __restrict__ bary,
     float* __restrict__ dists) {
     // staged face records, their face indices and the owners' records; the
     // output phase reuses the whole block for its key exchange
@@ -822,8 +839,9 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
     OwnerRec* orec = reinterpret_cast<OwnerRec*>(stage + kFineThreads * (sizeof(FaceRec) + 4));
     // the round's masks
     __shared__ __align__(16) unsigned char aux[2 * kBin * (kFineThreads / 64) * 8];
-    __shared__ uint16_t pcode[kPairWin];
-    __shared__ double pres[kPairWin];
+    constexpr int kWin = KMAX <= 2 ? kPairWinSmallK : kPairWin;
+    __shared__ uint16_t pcode[kWin];
+    __shared__ double pres[kWin];
     __shared__ int32_t ofill[kFineThreads];
     __shared__ float pcx[kBin], pcy[kBin];   // pixel centres of the bin's columns and rows
     __shared__ int wsum[kFineThreads / 64];
@@ -875,7 +893,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         const int32_t cnt = count[b];
         const int64_t o = offset[b];
         const bool list_mode = (o + cnt <= capacity);
-        const bool sorted = list_sorted(o, cnt, capacity);
+        const bool sorted = list_sorted(o, cnt, capacity, sort_min);
         const float* lb = round_lb + b * kRoundsPerBin;
         int64_t f0 = off[n], f1 = off[n + 1];
         f0 = f0 < 0 ? 0 : f0;
@@ -984,7 +1002,7 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             }
             int active = __syncthreads_count(left > 0);
             while (active > 0) {
-                const int cap = kPairWin / active;
+                const int cap = kWin / active;
                 const int take = left < cap ? left : cap;
                 left -= take;
                 int packed_total;
@@ -1120,12 +1138,14 @@ static void launch_fine(const FwdArgs& a, dim3 grid, const FaceRec* recs, const 
                         const float* round_lb) {
     if (a.settings & DMR_RASTER_PERSPECTIVE_CORRECT)
         fine_raster<KMAX, true><<<grid, kFineThreads, 0, a.stream>>>(
-            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
-            a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
+            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, sort_min_entries(a.K),
+            a.H, a.W, a.K, a.blur, a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary,
+            a.dists);
     else
         fine_raster<KMAX, false><<<grid, kFineThreads, 0, a.stream>>>(
-            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, a.H, a.W, a.K, a.blur,
-            a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary, a.dists);
+            recs, fbin, a.F, a.off, count, offset, items, hdr, entries, round_lb, a.capacity, sort_min_entries(a.K),
+            a.H, a.W, a.K, a.blur, a.settings, (int32_t)a.L.nbx, (int32_t)a.L.nby, a.pix_to_face, a.zbuf, a.bary,
+            a.dists);
 }
 
 hipError_t launch_binning(const FwdArgs& a, bool sort) {
@@ -1164,7 +1184,7 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     // heavy bins are split into quarter items for the mesh fine pass only
     const int split = (a.K <= kSplitMaxK && !a.points) ? 1 : 0;
     bin_scan<<<1, kScanThreads, 0, a.stream>>>(count, offset, rep, count_replicas(a.L.bins), perm, items, a.L.bins,
-                                                 split, block_live,
+                                                 split, sort_min_entries(a.K), block_live,
                                                  a.F > 0 ? a.L.setup_blocks : 0, a.capacity, a.L.min_bytes, hdr);
     timing_end(kKBinScan, a.stream);
     if (a.F > 0) {
@@ -1177,7 +1197,7 @@ hipError_t launch_binning(const FwdArgs& a, bool sort) {
     if (a.F > 0 && sort) {
         timing_begin(kKBinSort, a.stream);
         bin_sort<<<(unsigned)a.L.bins, kSortThreads, 0, a.stream>>>(fbin, count, offset, perm, entries, a.capacity,
-                                                                     round_lb);
+                                                                     sort_min_entries(a.K), hdr, round_lb);
         timing_end(kKBinSort, a.stream);
     }
     return hipGetLastError();
@@ -1195,7 +1215,10 @@ hipError_t launch_forward(const FwdArgs& a) {
     uint32_t* items = reinterpret_cast<uint32_t*>(ws + a.L.off_items);
     float* round_lb = reinterpret_cast<float*>(ws + a.L.off_roundlb);
     int32_t* entries = reinterpret_cast<int32_t*>(ws + a.L.off_entries);
-    // room for every item: four per bin when bins may be split
+    // room for every item: four per bin when bins may be split (a loop over
+    // items on a smaller grid would save the empty workgroups' few
+    // microseconds, but its live state spills scalar registers: measured
+    // slower)
     dim3 grid((unsigned)(a.L.bins * (a.K <= kSplitMaxK ? 4 : 1)));
     timing_begin(kKFineRaster, a.stream);
 #define DMR_FINE(KM) launch_fine<KM>(a, grid, recs, fbin, count, offset, items, hdr, entries, round_lb)
