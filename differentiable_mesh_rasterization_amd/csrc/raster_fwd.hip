@@ -222,13 +222,66 @@ __device__ __forceinline__ int64_t block_exclusive_sum64(int64_t v, int64_t* wsu
     return r;
 }
 
-// Sum over a kScanThreads workgroup (wave sums, one LDS atomic per wave).
-__device__ __forceinline__ int64_t block_sum64(int64_t v, unsigned long long* acc) {
-    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
-    if ((threadIdx.x & 63) == 0) atomicAdd(acc, (unsigned long long)v);
+// Sums of two values over a kScanThreads workgroup (wave sums, one LDS
+// atomic per wave and value, one barrier).
+__device__ __forceinline__ void block_sum64x2(int64_t& a, int64_t& b, unsigned long long* acc) {
+    for (int d = 32; d >= 1; d >>= 1) {
+        a += __shfl_xor(a, d, 64);
+        b += __shfl_xor(b, d, 64);
+    }
+    if ((threadIdx.x & 63) == 0) {
+        atomicAdd(&acc[0], (unsigned long long)a);
+        atomicAdd(&acc[1], (unsigned long long)b);
+    }
     __syncthreads();
-    const int64_t r = (int64_t)*acc;
-    return r;
+    a = (int64_t)acc[0];
+    b = (int64_t)acc[1];
+}
+
+// Lanes below this one among the lanes of mask m.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Adds one per active lane to the LDS counter arr[key] and returns each
+// active lane's place (the counter's value before its unit). The lanes that
+// share the key of the first active lane add with one atomic (the weight
+// buckets of neighbouring bins are mostly the same, and a wave's atomics on
+// one LDS address serialise); the others add one each.
+__device__ __forceinline__ int32_t lds_take(int32_t* arr, int32_t key, bool active) {
+    const uint64_t act = __ballot(active);
+    if (act == 0) return 0;
+    const int lane = threadIdx.x & 63;
+    const int leader = __builtin_ctzll(act);
+    const int32_t k = __builtin_amdgcn_readlane(key, leader);
+    const bool same = active && key == k;
+    const uint64_t m = __ballot(same);
+    int32_t base = 0, own = 0;
+    if (lane == leader) base = atomicAdd(&arr[k], (int32_t)__popcll(m));
+    if (active && !same) own = atomicAdd(&arr[key], 1);
+    base = __builtin_amdgcn_readlane(base, leader);
+    return same ? base + lanes_below(m) : own;
+}
+
+// Loads v[g..g+3] (entries at or past `end` read as 0): one 16-byte load
+// when the four are whole and aligned.
+__device__ __forceinline__ void load4(const int32_t* __restrict__ v, int64_t g, int64_t end, bool vec, int32_t (&c)[4]) {
+    if (vec && g + 4 <= end) {
+        const int4 x = *reinterpret_cast<const int4*>(v + g);
+        c[0] = x.x; c[1] = x.y; c[2] = x.z; c[3] = x.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) c[k] = g + k < end ? v[g + k] : 0;
+    }
+}
+__device__ __forceinline__ void store4(int32_t* __restrict__ v, int64_t g, int64_t end, bool vec, const int32_t (&c)[4]) {
+    if (vec && g + 4 <= end) {
+        *reinterpret_cast<int4*>(v + g) = make_int4(c[0], c[1], c[2], c[3]);
+    } else {
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            if (g + k < end) v[g + k] = c[k];
+    }
 }
 
 __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ count,
@@ -240,7 +293,7 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
                                                          int64_t nblocks, int64_t capacity, size_t base_bytes,
                                                          WsHeader* __restrict__ hdr) {
     __shared__ int64_t wsum[kScanThreads / 64 + 1];
-    __shared__ unsigned long long acc_ovf, acc_live;
+    __shared__ unsigned long long acc[2];
     __shared__ int32_t bucket_n[kOrderBuckets];
     __shared__ int32_t bucket_at[kOrderBuckets];
     __shared__ int32_t item_n[kOrderBuckets];
@@ -250,35 +303,51 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
         bucket_n[t] = 0;
         item_n[t] = 0;
     }
-    if (t == 0) {
-        acc_ovf = 0;
-        acc_live = 0;
-    }
-    // each bin's count is the sum of its copies; their running sums become
-    // the copies' fill cursors (copy r's faces follow those of copies < r)
-    for (int64_t b = t; b < bins; b += kScanThreads) {
-        int32_t cr[kCountReplicas];
-#pragma unroll
-        for (int r = 0; r < kCountReplicas; ++r) cr[r] = r < replicas ? rep[(int64_t)r * bins + b] : 0;
-        int32_t c = 0;
+    if (t < 2) acc[t] = 0;
+    // Thread t owns the bins [b0, b1), in groups of four (16-byte accesses
+    // where bins is a multiple of four, so that every copy's groups are
+    // aligned).
+    const int64_t per = (((bins + kScanThreads - 1) / kScanThreads) + 3) & ~(int64_t)3;
+    const int64_t b0 = min(bins, (int64_t)t * per);
+    const int64_t b1 = min(bins, b0 + per);
+    const bool vec = (bins & 3) == 0;
+    // the live-face counts of the setup blocks, loaded ahead
+    int64_t lv = 0;
+    for (int64_t q = t; q < nblocks; q += kScanThreads) lv += block_live[q];
+    __syncthreads();   // the bucket counters are zero
+    // Each bin's count is the sum of its copies; their running sums become
+    // the copies' fill cursors (copy r's faces follow those of copies < r).
+    // The bins and items are counted into their weight buckets.
+    int64_t s = 0;
+    for (int64_t g = b0; g < b1; g += 4) {
+        int32_t cr[kCountReplicas][4];
 #pragma unroll
         for (int r = 0; r < kCountReplicas; ++r) {
-            if (r < replicas) rep[(int64_t)r * bins + b] = c;
-            c += cr[r];
+            if (r < replicas) load4(rep + (int64_t)r * bins, g, b1, vec, cr[r]);
         }
-        count[b] = c;
-    }
-    const int64_t per = (bins + kScanThreads - 1) / kScanThreads;
-    const int64_t b0 = t * per;
-    const int64_t b1 = min(bins, b0 + per);
-    int64_t s = 0;
-    __syncthreads();
-    for (int64_t b = b0; b < b1; ++b) {
-        const int32_t c = count[b];
-        s += c;
-        atomicAdd(&bucket_n[order_bucket(c)], 1);
-        const bool split = allow_split && c >= kSplitMin;
-        atomicAdd(&item_n[order_bucket(split ? c / 4 : c)], split ? 4 : 1);
+        int32_t c[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int r = 0; r < kCountReplicas; ++r) {
+            if (r < replicas) {
+                int32_t cur[4];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {
+                    cur[k] = c[k];
+                    c[k] += cr[r][k];
+                }
+                store4(rep + (int64_t)r * bins, g, b1, vec, cur);
+            }
+        }
+        store4(count, g, b1, vec, c);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool valid = g + k < b1;
+            s += c[k];
+            const bool split = valid && allow_split && c[k] >= kSplitMin;
+            lds_take(bucket_n, order_bucket(c[k]), valid);
+            lds_take(item_n, order_bucket(c[k]), valid && !split);
+            if (split) atomicAdd(&item_n[order_bucket(c[k] / 4)], 4);
+        }
     }
     int64_t total = 0;
     int64_t run = block_exclusive_sum64(s, wsum, total);   // synchronises: the bucket counts are complete
@@ -307,25 +376,34 @@ __global__ __launch_bounds__(kScanThreads) void bin_scan(int32_t* __restrict__ c
         if (t == order_bucket(sort_min + 1)) hdr->sort_bins = x;
     }
     __syncthreads();
+    // list offsets, the sort order and the fine pass's items
     int64_t over = 0;
-    for (int64_t b = b0; b < b1; ++b) {
-        offset[b] = run;
-        const int32_t c = count[b];
-        if (run + c > capacity) ++over;
-        run += c;
-        perm[atomicAdd(&bucket_at[order_bucket(c)], 1)] = (int32_t)b;
-        const uint32_t code = (uint32_t)b << 3;
-        if (allow_split && c >= kSplitMin) {
-            const int at = atomicAdd(&item_at[order_bucket(c / 4)], 4);
-            for (int q = 0; q < 4; ++q) items[at + q] = code | (uint32_t)q;
-        } else {
-            items[atomicAdd(&item_at[order_bucket(c)], 1)] = code | (uint32_t)kItemWhole;
+    for (int64_t g = b0; g < b1; g += 4) {
+        int32_t c[4];
+        load4(count, g, b1, vec, c);   // this thread's own stores above
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int64_t b = g + k;
+            const bool valid = b < b1;
+            if (valid) {
+                offset[b] = run;
+                if (run + c[k] > capacity) ++over;
+                run += c[k];
+            }
+            const bool split = valid && allow_split && c[k] >= kSplitMin;
+            const int32_t pos = lds_take(bucket_at, order_bucket(c[k]), valid);
+            const int32_t at = lds_take(item_at, order_bucket(c[k]), valid && !split);
+            const uint32_t code = (uint32_t)b << 3;
+            if (valid) perm[pos] = (int32_t)b;
+            if (valid && !split) items[at] = code | (uint32_t)kItemWhole;
+            if (split) {
+                const int a4 = atomicAdd(&item_at[order_bucket(c[k] / 4)], 4);
+                for (int q = 0; q < 4; ++q) items[a4 + q] = code | (uint32_t)q;
+            }
         }
     }
-    int64_t lv = 0;
-    for (int64_t q = t; q < nblocks; q += kScanThreads) lv += block_live[q];
-    const int64_t o = block_sum64(over, &acc_ovf);
-    const int64_t live = block_sum64(lv, &acc_live);
+    int64_t o = over, live = lv;
+    block_sum64x2(o, live, acc);
     if (t == 0) {
         hdr->live_faces = live;
         offset[bins] = total;
