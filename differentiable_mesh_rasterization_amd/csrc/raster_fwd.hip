@@ -841,6 +841,28 @@ __device__ __forceinline__ int block256_exclusive_sum_total(int v, int* wsum, in
     return before + x - v;
 }
 
+// Padding of `rows` rows of an output array whose slots are all empty: the
+// run of run_words 32-bit words of row r starts at word first + r *
+// row_words and takes `pattern` (all ones for an index of -1, the bits of
+// -1.0f for a value). Sixteen threads share a row, with 16-byte stores when
+// the array and its rows are 16-byte aligned.
+__device__ __forceinline__ void pad_rows(uint32_t* __restrict__ base, int64_t first, int64_t row_words, int rows,
+                                         int run_words, uint32_t pattern) {
+    const int r = threadIdx.x >> 4, c0 = threadIdx.x & 15;
+    if (r >= rows) return;
+    uint32_t* row = base + first + (int64_t)r * row_words;
+    const bool aligned = (reinterpret_cast<uintptr_t>(base) & 15) == 0 && (row_words & 3) == 0;
+    int c = c0;
+    if (aligned) {
+        const int chunks = run_words >> 2;
+        const uint4 v = make_uint4(pattern, pattern, pattern, pattern);
+        uint4* row4 = reinterpret_cast<uint4*>(row);
+        for (; c < chunks; c += 16) row4[c] = v;
+        c = (chunks << 2) + c0;
+    }
+    for (; c < run_words; c += 16) row[c] = pattern;
+}
+
 // A face record staged piece-major in LDS.
 __device__ __forceinline__ FaceRec staged_rec(const int4* s, uint32_t u) {
     FaceRec r;
@@ -978,6 +1000,22 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
         f1 = f1 > F ? F : f1;
         const int64_t total = list_mode ? (int64_t)cnt : (f1 > f0 ? f1 - f0 : 0);
         bool done = !valid;
+
+        // A bin with no face (a whole item: split bins have many) has every
+        // slot empty: its region is padded row by row, with no keys, lists
+        // or slot arithmetic. Such items come last in the queue and form
+        // the pass's tail.
+        if (total == 0) {
+            const int rows = min(kBin, H - by * kBin), cols = min(kBin, W - bx * kBin);
+            const int64_t px0 = ((int64_t)n * H + by * kBin) * W + bx * kBin;   // the region's first pixel
+            const int64_t wk = (int64_t)W * K;
+            const uint32_t none = __float_as_uint(-1.0f);
+            pad_rows(reinterpret_cast<uint32_t*>(pix_to_face), 2 * px0 * K, 2 * wk, rows, 2 * cols * K, 0xffffffffu);
+            pad_rows(reinterpret_cast<uint32_t*>(zbuf), px0 * K, wk, rows, cols * K, none);
+            pad_rows(reinterpret_cast<uint32_t*>(bary), 3 * px0 * K, 3 * wk, rows, 3 * cols * K, none);
+            pad_rows(reinterpret_cast<uint32_t*>(dists), px0 * K, wk, rows, cols * K, none);
+            return;
+        }
 
         // The next round's list entry is loaded once this round's records
         // are staged, and its box at the round's end, so that a round waits
@@ -1189,16 +1227,23 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
                         (uint16_t)e;
             }
             __syncthreads();
+            // (each thread's next slot's record is loaded while the current
+            // one is evaluated: in a dense bin most slots are filled, and a
+            // chain of dependent record gathers made the output stage of the
+            // longest items as long as two of their rounds)
             const int nf = nfill;
+            FaceRec rnext;
+            if (t < nf) rnext = recs[(int32_t)(kbuf[olist[t]] & 0xffffffffull)];
             for (int x = t; x < nf; x += kFineThreads) {
                 const int e = olist[x];
+                const FaceRec rcur = rnext;
+                if (x + kFineThreads < nf) rnext = recs[(int32_t)(kbuf[olist[x + kFineThreads]] & 0xffffffffull)];
                 const int rr = (int)__umulhi((uint32_t)e, m_row);
                 const int within = e - rr * row_slots;
                 const int jj = K > 1 ? (int)__umulhi((uint32_t)within, m_k) : within;
                 const int64_t so = (row0 + (int64_t)(ra + rr) * W) * K + within;
-                const int32_t face = (int32_t)(kbuf[e] & 0xffffffffull);
                 float o0, o1, o2, sd;
-                slot_outputs<PERSP>(recs[face], pcx[reg_c + jj], pcy[reg_r + ra + rr],
+                slot_outputs<PERSP>(rcur, pcx[reg_c + jj], pcy[reg_r + ra + rr],
                                     (settings & DMR_RASTER_UNCLIPPED_BARY) != 0, o0, o1, o2, sd);
                 bary[3 * so + 0] = o0;
                 bary[3 * so + 1] = o1;
