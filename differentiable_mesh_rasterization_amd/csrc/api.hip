@@ -121,6 +121,12 @@ dmr_status check_geometry(const float* verts, int64_t V, const int64_t* faces, i
 
 }  // namespace
 
+// The kernels read the workspace's per-face records and bin tables with
+// 16-byte vector accesses at 256-byte aligned offsets from its start.
+static bool ws_aligned(const void* workspace) {
+    return (reinterpret_cast<uintptr_t>(workspace) & 15) == 0;
+}
+
 extern "C" {
 
 const char* dmr_status_string(dmr_status s) {
@@ -177,6 +183,7 @@ dmr_status rasterize_meshes_fwd_ex(const float* verts, int64_t V, const int64_t*
     // work items of the fine pass are bin << 3 | part in 32 bits, four per bin at most
     if (L.bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < L.min_bytes) return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    if (!ws_aligned(workspace)) return DMR_ERROR_INVALID_VALUE;
     int64_t cap = (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t));
     if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
 
@@ -275,6 +282,7 @@ dmr_status rasterize_meshes_bwd(const float* verts, int64_t V, const int64_t* fa
     const bool reuse = (flags & DMR_BWD_REUSE_FORWARD_WORKSPACE) != 0;
     if (reuse && slots > 0 && (workspace == nullptr || workspace_bytes < L.min_bytes))
         return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    if (reuse && slots > 0 && !ws_aligned(workspace)) return DMR_ERROR_INVALID_VALUE;
     int64_t cap = (reuse && slots > 0) ? (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t)) : 0;
     if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
     BwdArgs a;
@@ -427,6 +435,7 @@ dmr_status rasterize_points_fwd(const float* points, int64_t P, const int64_t* c
     FwdLayout L = fwd_layout(N, P, H, W, sizeof(PointRec));
     if (L.bins >= ((int64_t)1 << 28)) return DMR_ERROR_UNSUPPORTED;
     if (workspace == nullptr || workspace_bytes < L.min_bytes) return DMR_ERROR_WORKSPACE_TOO_SMALL;
+    if (!ws_aligned(workspace)) return DMR_ERROR_INVALID_VALUE;
     int64_t cap = (int64_t)((workspace_bytes - L.min_bytes) / sizeof(int32_t));
     if (cap > (int64_t)INT32_MAX) cap = INT32_MAX;
     FwdArgs a{};

@@ -108,9 +108,11 @@ typedef enum dmr_status {
  *   bary       [N,H,W,K,3] float32  clipped, renormalised barycentrics; -1 pads.
  *   dists      [N,H,W,K]   float32  signed squared distance to the face's
  *                                   edges (< 0 inside); -1 on padding.
- *   workspace  device scratch of workspace_bytes >= dmr_workspace_min_size();
- *              dmr_workspace_size_hint() gives a size that normally holds the
- *              per-bin face lists. Results do not depend on the size: bins
+ *   workspace  device scratch of workspace_bytes >= dmr_workspace_min_size(),
+ *              16-byte aligned (else DMR_ERROR_INVALID_VALUE; hipMalloc and
+ *              torch allocations are); dmr_workspace_size_hint() gives a
+ *              size that normally holds the per-bin face lists. Results do
+ *              not depend on the size: bins
  *              whose list does not fit are rasterised from their mesh's full
  *              face range instead (exact, slower), and the size that would
  *              have held every list is recorded (dmr_workspace_stats).
@@ -177,9 +179,10 @@ dmr_status rasterize_meshes_fwd_noalloc(const float* verts, int64_t V, const int
  *              records replace recomputing each face's data from verts and
  *              faces, and its bin order and counts schedule the tiles (bins
  *              without faces are skipped). The caller guarantees this; it is
- *              not checked, and any other content gives wrong gradients. The
- *              call only reads the workspace. Without that bit the workspace
- *              is not used and may be NULL.
+ *              not checked (only its size and 16-byte alignment are), and any
+ *              other content gives wrong gradients. The call only reads the
+ *              workspace. Without that bit the workspace is not used and may
+ *              be NULL.
  * Contributions are summed per 16x16 tile and vertex in LDS, in 64-bit fixed
  * point relative to each sum's own scale (units of 2^-30 of the largest
  * partial of the slot that started it), so the accuracy does not depend on

@@ -99,6 +99,7 @@ def _bwd(lib, **kw):
     (dict(N=1 << 40, H=30000, W=30000, K=64), UNSUPPORTED),
     (dict(F=1 << 31), UNSUPPORTED),
     (dict(ws=None), WS_SMALL), (dict(ws_bytes=100), WS_SMALL),
+    (dict(ws=ctypes.c_void_p(0x1004), ws_bytes=1 << 30), INVALID),   # workspace not 16-byte aligned
 ])
 def test_forward_rejects_invalid_arguments(dmr, kw, status):
     assert _fwd(dmr.lib(), **kw) == status
@@ -126,6 +127,7 @@ def test_forward_with_nothing_to_draw_is_a_no_op(dmr):
     (dict(gv=None), INVALID), (dict(p2f=None), INVALID), (dict(faces=None), INVALID),
     (dict(blur=-1.0), INVALID), (dict(blur=float("nan")), INVALID), (dict(flags=0x10), INVALID), (dict(flags=0x80000000), INVALID),
     (dict(ws=None, flags=1), WS_SMALL), (dict(ws_bytes=100, flags=1), WS_SMALL),
+    (dict(ws=ctypes.c_void_p(0x1008), flags=1), INVALID),   # forward workspace not 16-byte aligned
 ])
 def test_backward_rejects_invalid_arguments(dmr, kw, status):
     assert _bwd(dmr.lib(), **kw) == status
