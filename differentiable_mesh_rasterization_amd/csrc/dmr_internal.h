@@ -20,8 +20,10 @@ namespace dmr {
 constexpr int kBin = 16;
 constexpr int kBinPixels = kBin * kBin;
 constexpr int kFineThreads = kBinPixels;
-// Faces per setup/fill workgroup.
+// Faces per setup/fill workgroup (kSetupThreadsWide for triangle soups; the
+// workspace holds a live count per workgroup of the smaller size).
 constexpr int kSetupThreads = 256;
+constexpr int kSetupThreadsWide = 512;
 // Bin lists of more than one round and up to kSortMax faces are ordered by
 // depth lower bound; each such list has kSortMax / kFineThreads per-round
 // depth bounds. A list of one round (at most kSortMin entries) is left as
