@@ -918,9 +918,9 @@ struct OwnerRec {
 // slot-linearly (lane q writes slot q of the row's contiguous run) after the
 // keys are exchanged through LDS, so that stores are contiguous across lanes.
 constexpr int kPairWin = 1536;
-// For K <= 2 the windows hold half as many pairs (measured faster on the
-// 1M-triangle soup at K = 1; a fifth workgroup per CU, which the smaller
-// LDS footprint would allow, changed nothing).
+// For K <= 2 the pair buffers hold half as many entries (those passes
+// evaluate their pairs in per-owner loops; the buffers serve the output
+// stage's lists).
 constexpr int kPairWinSmallK = 768;
 constexpr int kLaneMinPairs = 24;    // a dense round: at least kLaneMinOwners owners
 constexpr int kLaneMinOwners = 240;  // with at least kLaneMinPairs candidate pairs each
@@ -1104,7 +1104,12 @@ __global__ __launch_bounds__(kFineThreads) __attribute__((amdgpu_waves_per_eu(KM
             // wave then have similar trip counts, and each pair is tested
             // against its owner's current bound, which prunes more where a
             // push costs two instructions per list slot.
-            if (KMAX >= 16 && __syncthreads_count(left >= kLaneMinPairs) >= kLaneMinOwners) {
+            // For K <= 2 every round takes the per-owner loops: a pair's push
+            // is one or two instructions, and the windows' codes, prefix sums
+            // and LDS indirection cost more per pair than the lanes that a
+            // loop's uneven trip counts leave idle (1M-triangle soup, K = 1:
+            // 102.8 -> 95.1 us; at K = 8 the windows stay faster).
+            if (KMAX <= 2 || (KMAX >= 16 && __syncthreads_count(left >= kLaneMinPairs) >= kLaneMinOwners)) {
                 const uint64_t mw[4] = {m0, m1, m2, m3};
 #pragma unroll 1
                 for (int w = 0; w < 4; ++w) {

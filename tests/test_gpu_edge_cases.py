@@ -231,6 +231,20 @@ def all_faces_cover_a_split_bin_k16():
 
 
 @case
+def all_faces_cover_a_split_bin_k1():
+    # quarter items at K = 1, whose rounds always take the per-owner loops:
+    # each owner keeps its own nearest face and the quad's are merged
+    v, f = _covering(26, 2400)
+    return v, f, [0, 2400], 16, 16, 1, 0.0
+
+
+@case
+def all_faces_cover_a_split_bin_k2():
+    v, f = _covering(27, 2200)
+    return v, f, [0, 2200], 16, 16, 2, 1e-4
+
+
+@case
 def tiny_positive_depths():
     # depths down to binary32 subnormals: their keys read as binary64 are
     # subnormal too, and must still order exactly
