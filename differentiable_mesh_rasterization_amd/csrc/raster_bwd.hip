@@ -368,8 +368,14 @@ __global__ __launch_bounds__(kBwdThreads) void backward_slots(
         const int32_t f_idle = (f_last >= 0 && (int64_t)f_last < F) ? f_last : 0;
         for (int e0 = 0; e0 < m; e0 += 2 * kBwdThreads) {
             SlotIn in[2];
+            // the second slot only where this pass of the list has one
+            // (uniform: a tile of fewer filled slots than threads takes one
+            // slot per thread, without the second's cooperative loads)
+            const int nu = (e0 + kBwdThreads < m) ? 2 : 1;
+            in[1].ok = false;
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
+                if (u >= nu) break;
                 const int x = e0 + t + u * kBwdThreads;
                 const int64_t f = x < m ? (int64_t)lface[x] : -1;
                 in[u].ok = f >= 0 && f < F;
