@@ -174,6 +174,39 @@ inline FwdLayout fwd_layout(int64_t N, int64_t F, int32_t H, int32_t W, size_t r
     return L;
 }
 
+// 16-byte pieces of 64-byte records moved within an aligned lane quad: a
+// DPP permutation of the quad's four lanes, and the 4x4 transpose of pieces
+// and lanes. Before the transpose w[4k + c] is dword c of piece k of this
+// lane's record; after it, dword c of piece p (this lane's position in the
+// quad) of quad lane k's record, and the other way round (the transpose is
+// its own inverse). Two rounds: where lane bit b and piece bit b differ, a
+// lane takes the element of piece k ^ 2^b held by lane p ^ 2^b. All lanes of
+// the quad must take part.
+template <int CTRL>
+__device__ __forceinline__ int quad_perm(int v) {
+    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
+}
+__device__ __forceinline__ void quad_transpose(int (&w)[16]) {
+    const int p = threadIdx.x & 3;
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+        const int bit = 1 << b;
+        int t[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const bool take = ((p ^ k) & bit) != 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int o = w[4 * (k ^ bit) + c];
+                const int x = b == 0 ? quad_perm<0xb1>(o) : quad_perm<0x4e>(o);
+                t[4 * k + c] = take ? x : w[4 * k + c];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w[i] = t[i];
+    }
+}
+
 // Pixel centre coordinate for index j of an image side of size W.
 __device__ __forceinline__ float pixel_centre(int j, int W) {
     return (float)(2 * j + 1) / (float)W - 1.0f;

@@ -151,10 +151,6 @@ constexpr int kListCap = 1536;   // tile slots read (and at most compacted) per 
 // of quad permutations) leaves every lane with its own slot's record. All
 // lanes of the wave must take part; `f` is this lane's face, or any valid
 // face index when the lane has no slot.
-template <int CTRL>
-__device__ __forceinline__ int quad_perm(int v) {
-    return __builtin_amdgcn_mov_dpp(v, CTRL, 0xf, 0xf, false);
-}
 __device__ __forceinline__ FaceRec quad_load_record(const FaceRec* __restrict__ recs, int32_t f) {
     const int p = threadIdx.x & 3;
     // faces of the quad's four slots
@@ -173,26 +169,8 @@ __device__ __forceinline__ FaceRec quad_load_record(const FaceRec* __restrict__ 
         w[4 * k + 2] = v.z;
         w[4 * k + 3] = v.w;
     }
-    // transpose: afterwards w[4k + c] = dword c of piece k of this lane's
-    // slot. Round b takes, where lane bit b and piece bit b differ, the
-    // element of piece k ^ 2^b held by lane p ^ 2^b.
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int bit = 1 << b;
-        int t[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const bool take = ((p ^ k) & bit) != 0;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int o = w[4 * (k ^ bit) + c];
-                const int x = b == 0 ? quad_perm<0xb1>(o) : quad_perm<0x4e>(o);
-                t[4 * k + c] = take ? x : w[4 * k + c];
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w[i] = t[i];
-    }
+    // afterwards w[4k + c] = dword c of piece k of this lane's slot's record
+    quad_transpose(w);
     static_assert(sizeof(FaceRec) == 64, "record of four pieces");
     FaceRec r;
     r.x0 = __int_as_float(w[0]);
