@@ -556,8 +556,9 @@ __device__ __forceinline__ int block256_exclusive_sum(int v, int* wsum) {
 // list held in registers: entry q = t + kSortThreads * i).
 template <int PER, int NB>
 __device__ __forceinline__ void sort_list(const FaceBin* __restrict__ fbin, int32_t* __restrict__ entries, int64_t o,
-                                          int32_t cnt, float* __restrict__ lb, int32_t* hist, int* wsum,
-                                          uint32_t& lo_s, uint32_t& hi_s, uint32_t* rmin) {
+                                          int32_t cnt, float* __restrict__ lb, int32_t* hist, uint32_t* bmin,
+                                          int* wsum, uint32_t* wmin, uint32_t& lo_s, uint32_t& hi_s,
+                                          uint32_t* rmin) {
     constexpr int BPT = NB / kSortThreads;   // buckets per thread
     static_assert(NB % kSortThreads == 0 && NB <= kSortBuckets, "whole buckets per sort thread");
     const int t = threadIdx.x;
@@ -566,7 +567,10 @@ __device__ __forceinline__ void sort_list(const FaceBin* __restrict__ fbin, int3
         hi_s = 0u;
     }
 #pragma unroll
-    for (int i = 0; i < BPT; ++i) hist[t * BPT + i] = 0;
+    for (int i = 0; i < BPT; ++i) {
+        hist[t * BPT + i] = 0;
+        bmin[t * BPT + i] = 0xffffffffu;
+    }
     if (t < kRoundsPerBin) rmin[t] = 0xffffffffu;
     int32_t id[PER];
     uint32_t zb[PER];   // order bits of zmin
@@ -598,43 +602,71 @@ __device__ __forceinline__ void sort_list(const FaceBin* __restrict__ fbin, int3
         int k = (int)((order_bits_float(zb[i]) - lo) * scale);
         k = k < 0 ? 0 : (k >= NB ? NB - 1 : k);
         bk[i] = k;
-        if (t + kSortThreads * i < cnt) atomicAdd(&hist[k], 1);
+        if (t + kSortThreads * i < cnt) {
+            atomicAdd(&hist[k], 1);
+            atomicMin(&bmin[k], zb[i]);
+        }
     }
     __syncthreads();
-    // bucket starts: each thread owns BPT consecutive buckets
+    // Bucket starts (each thread owns BPT consecutive buckets), and the
+    // rounds' depth bounds: round r's bound is the smallest zmin of the
+    // bucket holding list position 256 r and of every later bucket, a lower
+    // bound on the zmin of every face from round r on (the sorted list
+    // holds no earlier bucket past that position). The buckets' minima come
+    // from atomics spread over all buckets; per-round atomics on at most 16
+    // counters had serialised the whole wave on one address.
     {
         int c[BPT];
+        uint32_t sm[BPT];   // suffix minima over this thread's buckets
         int local = 0;
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
             c[i] = hist[t * BPT + i];
             local += c[i];
+            sm[i] = bmin[t * BPT + i];
         }
-        int run = block256_exclusive_sum(local, wsum);
+#pragma unroll
+        for (int i = BPT - 2; i >= 0; --i) sm[i] = min(sm[i], sm[i + 1]);
+        // smallest bucket minimum of the threads after this one (a reverse
+        // scan: within the wave, then over the four waves)
+        const int lane = t & 63, wave = t >> 6;
+        uint32_t x = sm[0];
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t y = __shfl_down(x, d, 64);
+            if (lane + d < 64) x = min(x, y);
+        }
+        if (lane == 0) wmin[wave] = x;
+        uint32_t after = __shfl_down(x, 1, 64);   // suffix from the next lane
+        if (lane == 63) after = 0xffffffffu;
+        int run = block256_exclusive_sum(local, wsum);   // synchronises: wmin is complete
+#pragma unroll
+        for (int w = 0; w < kSortThreads / 64; ++w)
+            if (w > wave) after = min(after, wmin[w]);
 #pragma unroll
         for (int i = 0; i < BPT; ++i) {
+            // the rounds starting inside this bucket (a long bucket can hold
+            // several round starts)
+            for (int r = (run + kFineThreads - 1) / kFineThreads;
+                 c[i] > 0 && r * kFineThreads < run + c[i] && r < kRoundsPerBin; ++r)
+                rmin[r] = min(sm[i], after);
             hist[t * BPT + i] = run;
             run += c[i];
         }
     }
     __syncthreads();
     // Every entry has been read: scatter the ids to their sorted places in
-    // the list, and note each round's smallest depth bound.
+    // the list.
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
         if (t + kSortThreads * i < cnt) {
             const int pos = atomicAdd(&hist[bk[i]], 1);
             entries[o + pos] = id[i];
-            atomicMin(&rmin[pos / kFineThreads], zb[i]);
         }
     }
     __syncthreads();
-    // round r's bound: the smallest zmin of rounds r and later
-    if (t < kRoundsPerBin) {
-        uint32_t run = 0xffffffffu;
-        for (int r = t; r < kRoundsPerBin; ++r) run = min(run, rmin[r]);
-        lb[t] = (run == 0xffffffffu) ? __builtin_inff() : order_bits_float(run);
-    }
+    // round r's bound (a round past the list has none: +inf)
+    if (t < kRoundsPerBin) lb[t] = (rmin[t] == 0xffffffffu) ? __builtin_inff() : order_bits_float(rmin[t]);
 }
 
 __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restrict__ fbin,
@@ -645,7 +677,9 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
                                                          int32_t sort_min, const WsHeader* __restrict__ hdr,
                                                          float* __restrict__ round_lb) {
     __shared__ int32_t hist[kSortBuckets];
+    __shared__ uint32_t bmin[kSortBuckets];
     __shared__ int wsum[kSortThreads / 64];
+    __shared__ uint32_t wmin[kSortThreads / 64];
     __shared__ uint32_t lo_s, hi_s;
     __shared__ uint32_t rmin[kRoundsPerBin];
     // the bins past the order's prefix of sortable ones end at once
@@ -658,11 +692,11 @@ __global__ __launch_bounds__(kSortThreads) void bin_sort(const FaceBin* __restri
     // short lists (the common case) take a variant with fewer registers and
     // buckets
     if (cnt <= 2 * kSortThreads)
-        sort_list<2, kSortThreads>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
+        sort_list<2, kSortThreads>(fbin, entries, o, cnt, lb, hist, bmin, wsum, wmin, lo_s, hi_s, rmin);
     else if (cnt <= 4 * kSortThreads)
-        sort_list<4, kSortBuckets>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
+        sort_list<4, kSortBuckets>(fbin, entries, o, cnt, lb, hist, bmin, wsum, wmin, lo_s, hi_s, rmin);
     else
-        sort_list<kSortPer, kSortBuckets>(fbin, entries, o, cnt, lb, hist, wsum, lo_s, hi_s, rmin);
+        sort_list<kSortPer, kSortBuckets>(fbin, entries, o, cnt, lb, hist, bmin, wsum, wmin, lo_s, hi_s, rmin);
 }
 
 // ---------------------------------------------------------------------------
